@@ -1,0 +1,178 @@
+"""Pins for the oracle's layer forward (CPU only).
+
+The layer is tied to plain dense computations it must reduce to (a gated MLP
+written with torch in float64), to exact rational arithmetic, and to
+invariants: identical experts make the output independent of routing,
+x = 0 gives y = 0, scaling W2 by 2**n scales y by 2**n, relabelling experts
+changes nothing, shard outputs add up to the full output.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import scipy.special
+
+from oracle import moe as om
+from oracle import mx
+
+H, I, E, T = 64, 96, 4, 9
+
+
+def _weights(rng, E, I, H, fmt, std=0.02):
+    w1 = (rng.standard_normal((E, 2 * I, H)) * std).astype(np.float32)
+    w2 = (rng.standard_normal((E, H, I)) * std).astype(np.float32)
+    p1, s1 = om.quantize_weight(w1, fmt)
+    p2, s2 = om.quantize_weight(w2, fmt)
+    return p1, s1, p2, s2
+
+
+def _x(rng, T, H, scale=1.0):
+    x = torch.from_numpy((rng.standard_normal((T, H)) * scale).astype(np.float32)).to(torch.bfloat16)
+    return x.to(torch.float64).numpy()
+
+
+def _dense_mlp(a, d1, d2, act):
+    """Textbook gated MLP in torch float64: (silu(a Wg^T) * (a Wu^T)) W2^T,
+    with the intermediate passed through the pinned bf16 / MXFP8 rounding."""
+    a = torch.from_numpy(a)
+    wg = torch.from_numpy(d1[: d1.shape[0] // 2])
+    wu = torch.from_numpy(d1[d1.shape[0] // 2:])
+    h = torch.nn.functional.silu(a @ wg.T) * (a @ wu.T)
+    h = h.numpy()
+    if act == "bf16":
+        h = mx.round_to_bf16(h)
+    else:
+        c, s = mx.quantize(h, "e4m3")
+        h = mx.dequantize(c, s, "e4m3")
+    return (torch.from_numpy(h) @ torch.from_numpy(d2).T).numpy()
+
+
+def _act_input(x, act):
+    if act == "bf16":
+        return x
+    c, s = mx.quantize(x, "e4m3")
+    return mx.dequantize(c, s, "e4m3")
+
+
+@pytest.mark.parametrize("fmt,act", [("e2m1", "bf16"), ("e2m1", "mxfp8"), ("e3m2", "mxfp8")])
+def test_identical_experts_reduce_to_dense_mlp(fmt, act):
+    rng = np.random.default_rng(0)
+    p1, s1, p2, s2 = _weights(rng, 1, I, H, fmt)
+    P1, S1, P2, S2 = (np.repeat(a, E, axis=0) for a in (p1, s1, p2, s2))
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    y = om.moe_forward(x, lg, P1, S1, P2, S2, k=3, wfmt=fmt, act=act)["y"]
+    d1 = om.decode_weight(p1[0], s1[0], fmt, H)
+    d2 = om.decode_weight(p2[0], s2[0], fmt, I)
+    ref = _dense_mlp(_act_input(x, act), d1, d2, act)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_two_experts_weighting_per_slot():
+    """E = 2, k = 2: y = w_a * MLP_a + w_b * MLP_b with w = softmax of the two
+    logits (scipy); k = 1: y = MLP of the arg-max expert."""
+    rng = np.random.default_rng(1)
+    p1, s1, p2, s2 = _weights(rng, 2, I, H, "e2m1")
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, 2)).astype(np.float32)
+    dense = [_dense_mlp(x, om.decode_weight(p1[e], s1[e], "e2m1", H),
+                        om.decode_weight(p2[e], s2[e], "e2m1", I), "bf16") for e in range(2)]
+    y2 = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16")["y"]
+    p = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    assert np.allclose(y2, p[:, :1] * dense[0] + p[:, 1:] * dense[1], rtol=1e-12, atol=1e-14)
+    y1 = om.moe_forward(x, lg, p1, s1, p2, s2, k=1, wfmt="e2m1", act="bf16")["y"]
+    arg = np.where(lg[:, 1] > lg[:, 0], 1, 0)
+    assert np.allclose(y1, np.where(arg[:, None] == 1, dense[1], dense[0]), rtol=1e-12, atol=1e-14)
+
+
+def test_fc1_exact_rational():
+    """FC1 of decoded MX values is a sum of dyadic rationals: compare the
+    float64 product with exact Fraction arithmetic from the raw codes."""
+    rng = np.random.default_rng(2)
+    Hs, Is = 64, 32
+    p1, s1, _, _ = _weights(rng, 1, Is, Hs, "e2m1", std=1.0)
+    x = _x(rng, 3, Hs)
+    codes = mx.unpack(p1[0], "e2m1", Hs)
+    vals = {0: 0, 1: Fraction(1, 2), 2: 1, 3: Fraction(3, 2), 4: 2, 5: 3, 6: 4, 7: 6}
+    d1 = om.decode_weight(p1[0], s1[0], "e2m1", Hs)
+    z = x @ d1.T
+    for t in range(3):
+        for n in range(0, 2 * Is, 5):
+            acc = Fraction(0)
+            for kk in range(Hs):
+                c = int(codes[n, kk])
+                v = vals[c & 7] * (-1 if c & 8 else 1)
+                sc = Fraction(2) ** (int(s1[0, n, kk // 32]) - 127)
+                acc += Fraction(float(x[t, kk])) * v * sc
+            assert float(acc) == z[t, n]
+
+
+def test_zero_input_and_w2_power_of_two_scaling():
+    rng = np.random.default_rng(3)
+    p1, s1, p2, s2 = _weights(rng, E, I, H, "e2m1")
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    y0 = om.moe_forward(np.zeros((T, H)), lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16")["y"]
+    assert np.all(y0 == 0)
+    x = _x(rng, T, H)
+    y = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16")["y"]
+    y5 = om.moe_forward(x, lg, p1, s1, p2, (s2.astype(np.int64) + 5).astype(np.uint8),
+                        k=2, wfmt="e2m1", act="bf16")["y"]
+    assert np.array_equal(y5, y * 32.0)
+
+
+def test_expert_relabelling_invariance():
+    rng = np.random.default_rng(4)
+    p1, s1, p2, s2 = _weights(rng, E, I, H, "e3m2")
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    y = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e3m2", act="mxfp8")["y"]
+    perm = rng.permutation(E)
+    yp = om.moe_forward(x, lg[:, perm], p1[perm], s1[perm], p2[perm], s2[perm],
+                        k=2, wfmt="e3m2", act="mxfp8")["y"]
+    assert np.allclose(y, yp, rtol=1e-13, atol=1e-15)
+
+
+def test_shared_expert_adds_dense_mlp():
+    rng = np.random.default_rng(5)
+    p1, s1, p2, s2 = _weights(rng, E, I, H, "e3m2")
+    q1, r1, q2, r2 = _weights(rng, 1, 2 * I, H, "e3m2")
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    base = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e3m2", act="mxfp8")["y"]
+    both = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e3m2", act="mxfp8",
+                          shared=(q1[0], r1[0], q2[0], r2[0]))["y"]
+    dense = _dense_mlp(_act_input(x, "mxfp8"), om.decode_weight(q1[0], r1[0], "e3m2", H),
+                       om.decode_weight(q2[0], r2[0], "e3m2", 2 * I), "mxfp8")
+    assert np.allclose(both - base, dense, rtol=1e-10, atol=1e-13)
+
+
+def test_token_subset_and_precomputed_topk():
+    rng = np.random.default_rng(6)
+    p1, s1, p2, s2 = _weights(rng, E, I, H, "e2m1")
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    full = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16")
+    sub = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16", tokens=[7, 2])
+    assert np.array_equal(sub["y"], full["y"][[7, 2]])
+    given = om.moe_forward(x, None, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16",
+                           topk_ids=full["ids"], topk_w=full["w"])
+    assert np.array_equal(given["y"], full["y"])
+
+
+def test_expert_shards_sum_to_full_output():
+    rng = np.random.default_rng(7)
+    p1, s1, p2, s2 = _weights(rng, 8, I, H, "e2m1")
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, 8)).astype(np.float32)
+    full = om.moe_forward(x, lg, p1, s1, p2, s2, k=3, wfmt="e2m1", act="bf16")["y"]
+    parts = sum(om.moe_forward(x, lg, p1, s1, p2, s2, k=3, wfmt="e2m1", act="bf16",
+                               local_offset=2 * r, local_count=2)["y"] for r in range(4))
+    assert np.allclose(parts, full, rtol=1e-13, atol=1e-15)
+
+
+def test_silu_closed_forms():
+    g = np.array([0.0, 50.0, -50.0, 1.0, -800.0])
+    s = om.silu(g)
+    assert s[0] == 0.0 and abs(s[1] - 50.0) < 1e-15 * 50 and abs(s[2]) < 1e-19
+    assert abs(s[3] - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16 and s[4] == 0.0
