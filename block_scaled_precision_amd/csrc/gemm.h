@@ -1,0 +1,47 @@
+// Arguments of the grouped FC1 / FC2 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace moe_mx {
+
+struct FcArgs {
+  // M-tiles: routed mode reads `tiles[0 .. *num_tiles)`, grid sized for max_tiles;
+  // dense mode (dense_rows > 0) covers rows [0, dense_rows) of a single expert.
+  const Tile* tiles;
+  const int32_t* num_tiles;
+  int max_tiles;
+  int dense_rows;
+  // routed rows: permuted position p -> assignment a = t*k + j
+  const int32_t* sorted_assign;
+  int k;
+  const float* topk_w;  // FC2 routed: weight of assignment a
+  float dense_weight;   // FC2 dense: weight of every row
+  // A operand: FC1 -> x rows (bf16 [T, K] or E4M3 codes [T, K] + scales [T, K/32]),
+  //            FC2 -> h rows in permuted order (bf16 [P, K] or codes + scales)
+  const void* a;
+  const uint8_t* a_scale;
+  // B operand: weights [experts, N_w, K*bits/8] + scales [experts, N_w, K/32]
+  const uint8_t* w;
+  const uint8_t* w_scale;
+  int64_t w_estride;   // bytes per expert
+  int64_t ws_estride;  // scale bytes per expert
+  int K;               // contraction length (H for FC1, I for FC2)
+  int N;               // FC1: I (h columns); FC2: H
+  int nchunks;         // column chunks of N per M-tile
+  // outputs
+  void* out;           // FC1: h (bf16 [P, I] or E4M3 codes [P, I])
+  uint8_t* out_scale;  // FC1 MX: h scales [P, I/32]
+  float* y_acc;        // FC2: fp32 [T, H] accumulator
+};
+
+// Columns of N covered by one wave of the stream kernels.
+constexpr int kStreamColsFc1 = 32;
+constexpr int kStreamColsFc2 = 64;
+constexpr int kStreamRows = 16;
+
+hipError_t launch_fc_stream(const FcArgs& p, bool fc1, bool mx_act, int wfmt, hipStream_t st);
+
+}  // namespace moe_mx

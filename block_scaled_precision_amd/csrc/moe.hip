@@ -1,0 +1,352 @@
+// Host side of libmoe_mx: argument validation, architecture check, workspace
+// planning and the launch sequence of moe_fused, plus the public entry points
+// mx_quantize and moe_route.
+//
+// The boundary follows the pages' interfaces: the keyword call of the
+// TokenSpeed SiTU page ("Runtime API": physical intermediate size, global
+// expert count, local expert offset and count; "Supported contract": MXFP8
+// activations with a block-scale tensor, precomputed top-k), the op names of
+// the TokenSpeed-kernel page ("Public API": moe_route ... moe_fused), the
+// caller-owned, graph-safe workspaces of the mxfp6-sm120 page ("Execution
+// model", "Python API") and its fail-closed validation ("Validated scope").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "gemm.h"
+#include "internal.h"
+#include "mx_device.h"
+
+namespace moe_mx {
+
+// ------------------------------------------------------------------ arch ---
+
+moe_status_t check_arch() {
+  static std::atomic<int> cache[256];  // 0 unknown, 1 gfx950, 2 other
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_ARCH;
+  if (dev < 256) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 1) return MOE_OK;
+    if (c == 2) return MOE_ERR_ARCH;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_ARCH;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 256) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MOE_OK : MOE_ERR_ARCH;
+}
+
+// ------------------------------------------------------- small kernels ----
+
+__global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// y (bf16) = round-half-to-even of the fp32 accumulator
+__global__ __launch_bounds__(256) void k_finalize(const float4* __restrict__ acc, uint2* __restrict__ y,
+                                                  int64_t n4) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 v = acc[i];
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+    y[i] = make_uint2(lo, hi);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_copy_routing(const int32_t* __restrict__ ids_in,
+                                                      const float* __restrict__ w_in,
+                                                      int32_t* __restrict__ ids_out,
+                                                      float* __restrict__ w_out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  if (ids_out) ids_out[i] = ids_in[i];
+  if (w_out) w_out[i] = w_in[i];
+}
+
+static int64_t grid_for(int64_t n, int64_t per_block, int64_t cap) {
+  int64_t b = (n + per_block - 1) / per_block;
+  return b < 1 ? 1 : (b > cap ? cap : b);
+}
+
+// ------------------------------------------------------------ layouts ----
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static int wbits(mx_elem_t f) { return f == MX_E2M1 ? 4 : (f == MX_E3M2 ? 6 : 8); }
+
+struct FusedPlan {
+  int L, off;
+  int64_t A;
+  int nblk, max_tiles;
+  size_t ids, w, rank, hist, offsets, sorted, tiles, ntiles, xq, xs, h, hsc, hs, hssc, yacc, total;
+};
+
+static FusedPlan plan(const moe_problem_t& p) {
+  FusedPlan f;
+  f.off = p.local_expert_offset;
+  f.L = p.local_num_experts == 0 ? p.E : p.local_num_experts;
+  f.A = (int64_t)p.T * p.k;
+  f.nblk = (p.T + kTokensPerRouteBlock - 1) / kTokensPerRouteBlock;
+  f.max_tiles = (int)(f.A / kStreamRows + (f.A < f.L ? f.A : f.L));
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t r = o;
+    o = align_up(o + bytes, 256);
+    return r;
+  };
+  const bool mx = p.act == MOE_ACT_MXFP8;
+  const size_t T = (size_t)p.T, H = (size_t)p.H, I = (size_t)p.I, Is = (size_t)p.I_shared;
+  f.ids = take(f.A * 4);
+  f.w = take(f.A * 4);
+  f.rank = take(f.A * 4);
+  f.hist = take((size_t)f.nblk * f.L * 4);
+  f.offsets = take((size_t)(f.L + 1) * 4);
+  f.sorted = take(f.A * 4);
+  f.tiles = take((size_t)f.max_tiles * sizeof(Tile));
+  f.ntiles = take(4);
+  f.xq = mx ? take(T * H) : 0;
+  f.xs = mx ? take(T * H / 32) : 0;
+  f.h = take(f.A * I * (mx ? 1 : 2));
+  f.hsc = mx ? take(f.A * I / 32) : 0;
+  f.hs = Is ? take(T * Is * (mx ? 1 : 2)) : 0;
+  f.hssc = (Is && mx) ? take(T * Is / 32) : 0;
+  f.yacc = take(T * H * 4);
+  f.total = o;
+  return f;
+}
+
+static moe_status_t validate(const moe_problem_t* p, const moe_tensors_t* t) {
+  if (!p || !t) return MOE_ERR_INVALID_ARG;
+  if (p->T < 0 || p->H <= 0 || p->I <= 0 || p->I_shared < 0) return MOE_ERR_INVALID_ARG;
+  if (p->H % 32 || p->I % 32 || p->I_shared % 32) return MOE_ERR_INVALID_ARG;
+  if (p->E < 1 || p->E > kMaxExperts || p->k < 1 || p->k > p->E) return MOE_ERR_INVALID_ARG;
+  if (p->w_fmt != MX_E2M1 && p->w_fmt != MX_E3M2 && p->w_fmt != MX_E4M3) return MOE_ERR_INVALID_ARG;
+  if (p->act != MOE_ACT_BF16 && p->act != MOE_ACT_MXFP8) return MOE_ERR_INVALID_ARG;
+  const int L = p->local_num_experts == 0 ? p->E : p->local_num_experts;
+  if (p->local_expert_offset < 0 || L < 0 || (int64_t)p->local_expert_offset + L > p->E)
+    return MOE_ERR_INVALID_ARG;
+  if ((int64_t)p->T * p->k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  if (p->T > 0) {
+    if (!t->x || !t->y || !t->w1 || !t->w1_scale || !t->w2 || !t->w2_scale) return MOE_ERR_INVALID_ARG;
+    const bool have_in = t->topk_ids_in || t->topk_w_in;
+    if (have_in && !(t->topk_ids_in && t->topk_w_in)) return MOE_ERR_INVALID_ARG;
+    if (!have_in && !t->router_logits) return MOE_ERR_INVALID_ARG;
+    if (p->I_shared > 0 && (!t->ws1 || !t->ws1_scale || !t->ws2 || !t->ws2_scale)) return MOE_ERR_INVALID_ARG;
+    const void* ptrs[] = {t->x, t->y, t->w1, t->w1_scale, t->w2, t->w2_scale};
+    for (const void* q : ptrs)
+      if (!aligned16(q)) return MOE_ERR_INVALID_ARG;
+    if (p->I_shared > 0) {
+      const void* sp[] = {t->ws1, t->ws1_scale, t->ws2, t->ws2_scale};
+      for (const void* q : sp)
+        if (!aligned16(q)) return MOE_ERR_INVALID_ARG;
+    }
+  }
+  // valid, but outside what the kernels implement
+  if (p->w_fmt == MX_E4M3) return MOE_ERR_UNSUPPORTED;
+  if (p->w_fmt == MX_E3M2 && p->act == MOE_ACT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (p->H % 128 || p->I % 128 || p->I_shared % 128) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace moe_mx
+
+using namespace moe_mx;
+
+// ------------------------------------------------------- public entry points
+
+extern "C" const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_ARCH: return "no gfx950 device";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" const char* moe_mx_version(void) { return "0.1.0"; }
+
+extern "C" moe_status_t mx_quantize(const void* src, moe_src_t src_dtype, int64_t rows, int64_t cols,
+                                    int64_t src_ld, mx_elem_t fmt, uint8_t* codes, uint8_t* scales,
+                                    hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 || src_ld < cols) return MOE_ERR_INVALID_ARG;
+  if (src_dtype != MOE_SRC_BF16 && src_dtype != MOE_SRC_FP32) return MOE_ERR_INVALID_ARG;
+  if (fmt != MX_E2M1 && fmt != MX_E3M2 && fmt != MX_E4M3) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!src || !codes || !scales)) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  moe_status_t a = check_arch();
+  if (a != MOE_OK) return a;
+  return launch_quantize(src, src_dtype, rows, cols, src_ld, fmt, codes, scales, stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+extern "C" size_t moe_route_workspace_bytes(int32_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  const size_t nblk = ((size_t)T + kTokensPerRouteBlock - 1) / kTokensPerRouteBlock;
+  return align_up(nblk * E * 4, 256) + align_up((size_t)T * k * 4, 256) + 256;
+}
+
+extern "C" moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                                  float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || E < 1 || E > kMaxExperts || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_assign)) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)T * k > (int64_t)1 << 30) return MOE_ERR_UNSUPPORTED;
+  const size_t need = moe_route_workspace_bytes(T, E, k);
+  if (workspace_bytes < need || (!workspace && need > 0)) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_INVALID_ARG;
+  moe_status_t a = check_arch();
+  if (a != MOE_OK) return a;
+  const size_t nblk = ((size_t)T + kTokensPerRouteBlock - 1) / kTokensPerRouteBlock;
+  char* ws = (char*)workspace;
+  int32_t* hist = (int32_t*)ws;
+  int32_t* rank = (int32_t*)(ws + align_up(nblk * E * 4, 256));
+  if (launch_topk(logits, T, E, k, topk_ids, topk_w, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_permute(topk_ids, T, k, 0, E, hist, rank, expert_offsets, sorted_assign, nullptr, nullptr, 0,
+                     stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+extern "C" size_t moe_fused_workspace_bytes(const moe_problem_t* p) {
+  if (!p || p->T < 0 || p->E < 1 || p->k < 1 || p->H <= 0 || p->I <= 0 || p->I_shared < 0) return 0;
+  return plan(*p).total;
+}
+
+extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  moe_status_t v = validate(p, t);
+  if (v != MOE_OK) return v;
+  if (p->T == 0) return MOE_OK;
+  const FusedPlan f = plan(*p);
+  if (!workspace || workspace_bytes < f.total) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOE_ERR_INVALID_ARG;
+  moe_status_t a = check_arch();
+  if (a != MOE_OK) return a;
+
+  char* ws = (char*)workspace;
+  const bool mx = p->act == MOE_ACT_MXFP8;
+  const int wf = p->w_fmt == MX_E2M1 ? 1 : 2;
+  const int T = p->T, H = p->H, I = p->I, k = p->k, Is = p->I_shared;
+  float* yacc = (float*)(ws + f.yacc);
+  hipError_t e = hipSuccess;
+  auto ok = [&](hipError_t r) {
+    if (r != hipSuccess && e == hipSuccess) e = r;
+    return r == hipSuccess;
+  };
+
+  // fp32 accumulator <- 0 (a fill kernel, so the sequence stays graph-capturable)
+  const int64_t n4 = (int64_t)T * H / 4;
+  k_fill_zero<<<grid_for(n4, 256, 8192), 256, 0, stream>>>((float4*)yacc, n4);
+  if (!ok(hipGetLastError())) return MOE_ERR_HIP;
+
+  // 1. routing
+  const int32_t* ids;
+  const float* wts;
+  if (t->topk_ids_in) {
+    ids = t->topk_ids_in;
+    wts = t->topk_w_in;
+    if (t->topk_ids_out || t->topk_w_out) {
+      k_copy_routing<<<grid_for(f.A, 256, 1 << 30), 256, 0, stream>>>(ids, wts, t->topk_ids_out, t->topk_w_out, f.A);
+      if (!ok(hipGetLastError())) return MOE_ERR_HIP;
+    }
+  } else {
+    int32_t* ids_w = t->topk_ids_out ? t->topk_ids_out : (int32_t*)(ws + f.ids);
+    float* w_w = t->topk_w_out ? t->topk_w_out : (float*)(ws + f.w);
+    if (!ok(launch_topk(t->router_logits, T, p->E, k, ids_w, w_w, stream))) return MOE_ERR_HIP;
+    ids = ids_w;
+    wts = w_w;
+  }
+  // 2. permutation by local expert + tile list
+  int32_t* sorted = (int32_t*)(ws + f.sorted);
+  Tile* tiles = (Tile*)(ws + f.tiles);
+  int32_t* ntiles = (int32_t*)(ws + f.ntiles);
+  if (!ok(launch_permute(ids, T, k, f.off, f.L, (int32_t*)(ws + f.hist), (int32_t*)(ws + f.rank),
+                         (int32_t*)(ws + f.offsets), sorted, tiles, ntiles, kStreamRows, stream)))
+    return MOE_ERR_HIP;
+  // 3. MXFP8 activations
+  const uint8_t* xq = (const uint8_t*)(ws + f.xq);
+  const uint8_t* xs = (const uint8_t*)(ws + f.xs);
+  if (mx && !ok(launch_quantize(t->x, MOE_SRC_BF16, T, H, H, MX_E4M3, (uint8_t*)xq, (uint8_t*)xs, stream)))
+    return MOE_ERR_HIP;
+
+  const int64_t bytes_h = (int64_t)H * wbits(p->w_fmt) / 8;
+  const int64_t bytes_i = (int64_t)I * wbits(p->w_fmt) / 8;
+  // 4-5. FC1 + SiLU(gate)*up (+ MXFP8 requantization)
+  FcArgs a1 = {};
+  a1.tiles = tiles;
+  a1.num_tiles = ntiles;
+  a1.max_tiles = f.max_tiles;
+  a1.dense_rows = 0;
+  a1.sorted_assign = sorted;
+  a1.k = k;
+  a1.topk_w = wts;
+  a1.a = mx ? (const void*)xq : t->x;
+  a1.a_scale = xs;
+  a1.w = t->w1;
+  a1.w_scale = t->w1_scale;
+  a1.w_estride = 2 * (int64_t)I * bytes_h;
+  a1.ws_estride = 2 * (int64_t)I * (H / 32);
+  a1.K = H;
+  a1.N = I;
+  a1.nchunks = I / kStreamColsFc1;
+  a1.out = ws + f.h;
+  a1.out_scale = (uint8_t*)(ws + f.hsc);
+  if (!ok(launch_fc_stream(a1, true, mx, wf, stream))) return MOE_ERR_HIP;
+  // 6-7. FC2 + weighted combine into the fp32 accumulator
+  FcArgs a2 = a1;
+  a2.a = ws + f.h;
+  a2.a_scale = (const uint8_t*)(ws + f.hsc);
+  a2.w = t->w2;
+  a2.w_scale = t->w2_scale;
+  a2.w_estride = (int64_t)H * bytes_i;
+  a2.ws_estride = (int64_t)H * (I / 32);
+  a2.K = I;
+  a2.N = H;
+  a2.nchunks = H / kStreamColsFc2;
+  a2.out = nullptr;
+  a2.y_acc = yacc;
+  if (!ok(launch_fc_stream(a2, false, mx, wf, stream))) return MOE_ERR_HIP;
+  // shared expert: a dense expert over all T tokens with its own weight
+  if (Is > 0) {
+    const int64_t bytes_is = (int64_t)Is * wbits(p->w_fmt) / 8;
+    FcArgs s1 = a1;
+    s1.dense_rows = T;
+    s1.w = t->ws1;
+    s1.w_scale = t->ws1_scale;
+    s1.w_estride = 0;
+    s1.ws_estride = 0;
+    s1.N = Is;
+    s1.nchunks = Is / kStreamColsFc1;
+    s1.out = ws + f.hs;
+    s1.out_scale = (uint8_t*)(ws + f.hssc);
+    if (!ok(launch_fc_stream(s1, true, mx, wf, stream))) return MOE_ERR_HIP;
+    FcArgs s2 = a2;
+    s2.dense_rows = T;
+    s2.dense_weight = p->shared_weight;
+    s2.a = ws + f.hs;
+    s2.a_scale = (const uint8_t*)(ws + f.hssc);
+    s2.w = t->ws2;
+    s2.w_scale = t->ws2_scale;
+    s2.w_estride = 0;
+    s2.ws_estride = 0;
+    s2.K = Is;
+    s2.nchunks = H / kStreamColsFc2;
+    (void)bytes_is;
+    if (!ok(launch_fc_stream(s2, false, mx, wf, stream))) return MOE_ERR_HIP;
+  }
+  // 8. y = bf16(accumulator)
+  k_finalize<<<grid_for(n4, 256, 8192), 256, 0, stream>>>((const float4*)yacc, (uint2*)t->y, n4);
+  if (!ok(hipGetLastError())) return MOE_ERR_HIP;
+  return MOE_OK;
+}

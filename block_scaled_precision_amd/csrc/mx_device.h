@@ -1,0 +1,85 @@
+// Device helpers for OCP microscaling (MX) formats on gfx950.
+//
+// Formats (mxfp6-sm120 page, "Execution model": E4M3 activations and E3M2
+// weights with a UE8M0 scale per 32 K values; TokenSpeed SiTU page,
+// "Supported contract": MXFP4 E2M1 weights).  Field widths and biases are the
+// OCP MX v1.0 ones: E2M1 bias 1, E3M2 bias 3, E4M3 bias 7 (no infinities,
+// S.1111.111 is NaN), E8M0 = 2**(c-127).
+//
+// Encoding is done on the integer bits of fp32 values so that the result is
+// exactly "nearest element value, ties to the even code, saturate to the
+// largest finite value" for every finite input.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_mx {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Element format parameters: exponent bits, mantissa bits, bias, largest
+// finite magnitude code, emax (exponent of the largest finite value) and the
+// format operand code of the gfx950 scaled MFMA (0 = E4M3, 3 = E3M2, 4 = E2M1).
+template <int FMT> struct Fmt;
+template <> struct Fmt<1> { static constexpr int EB = 2, MB = 1, BIAS = 1, MAXC = 7,   EMAX = 2, BITS = 4, MFMA = 4; };
+template <> struct Fmt<2> { static constexpr int EB = 3, MB = 2, BIAS = 3, MAXC = 31,  EMAX = 4, BITS = 6, MFMA = 3; };
+template <> struct Fmt<3> { static constexpr int EB = 4, MB = 3, BIAS = 7, MAXC = 126, EMAX = 8, BITS = 8, MFMA = 0; };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round half to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// E8M0 code -> fp32 2**(c-127); code 0 is the fp32 subnormal 2**-127.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  return c ? __uint_as_float(c << 23) : __uint_as_float(0x00400000u);
+}
+
+// Shared exponent of a block from the bits of its largest magnitude:
+// clamp(floor(log2 amax) - emax, -127, 127); zero and fp32-subnormal maxima
+// give -127 (their floor(log2) is below -126, and emax >= 2).
+template <int FMT>
+__device__ __forceinline__ int block_exponent(uint32_t amax_bits) {
+  int E = (int)(amax_bits >> 23);
+  if (E == 0) return -127;
+  int s = E - 127 - Fmt<FMT>::EMAX;
+  return s < -127 ? -127 : s;  // E <= 254 keeps s <= 127 - emax
+}
+
+// 2**-s as an exact fp32 (|s| <= 127 and s <= 125 in use, so always normal).
+__device__ __forceinline__ float exp2_neg(int s) { return __uint_as_float((uint32_t)(127 - s) << 23); }
+
+// Nearest element code of q (already divided by the block scale).
+template <int FMT>
+__device__ __forceinline__ uint32_t encode(float q) {
+  using F = Fmt<FMT>;
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sign = (u >> 31) << (F::EB + F::MB);
+  const uint32_t mag = u & 0x7fffffffu;
+  const int E = (int)(mag >> 23);
+  if (E == 0) return sign;  // |q| < 2**-126: far below half of the smallest subnormal
+  const int e = E - 127;
+  const uint32_t sig = (mag & 0x7fffffu) | 0x800000u;  // 1.m * 2**23
+  constexpr int emin = 1 - F::BIAS;
+  const int shift = 23 - F::MB + (e < emin ? emin - e : 0);
+  if (shift > 25) return sign;  // below a quarter of the smallest subnormal
+  uint32_t kept = sig >> shift;
+  const uint32_t rem = sig & ((1u << shift) - 1u);
+  const uint32_t half = 1u << (shift - 1);
+  kept += (rem > half || (rem == half && (kept & 1u))) ? 1u : 0u;
+  uint32_t code = (e < emin) ? kept : ((uint32_t)(e + F::BIAS) << F::MB) + kept - (1u << F::MB);
+  code = code > (uint32_t)F::MAXC ? (uint32_t)F::MAXC : code;
+  return code | sign;
+}
+
+// SiLU(g) * u in fp32.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+}  // namespace moe_mx

@@ -1,0 +1,193 @@
+// Routing: softmax/top-k per token and the permutation of assignments by expert.
+//
+// top-k (mxfp6-sm120 page, table of paths: the routed path starts with
+// routing; fusedtok page: selection ties resolve to the earliest index):
+// one wave per token.  Each lane keeps E/64 logits; k rounds of a wave-wide
+// arg-max over 64-bit keys (order-preserving fp32 bits, then inverted id) pick
+// the experts in slot order, so equal logits go to the lower id.  The weights
+// are a softmax over the chosen logits in fp32 (the full softmax renormalised
+// over the chosen experts).
+//
+// Permutation (mxfp6-sm120 page, "Execution model": indirect routing) is a
+// deterministic counting sort with no global atomics on positions:
+//   1. per block of 64 tokens, an LDS bit mask per expert marks which lanes
+//      (tokens) chose it; popcount gives the block histogram, and the popcount
+//      below a lane gives the rank of its assignment inside the block;
+//   2. one block scans the histograms over blocks (write bases) and over
+//      experts (expert offsets), and emits the GEMM tile list;
+//   3. every assignment is written to base + rank.
+// The order inside an expert segment is therefore ascending token.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace moe_mx {
+
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// 4 waves per block, one token per wave; E <= 1024 -> at most 16 logits per lane.
+// Every lane sees the winner of each round, so all lanes carry the same
+// running softmax denominator; lane 0 writes ids and, in a second pass over
+// its own stores, the normalised weights.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  uint32_t key[16];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? ordered_bits(row[e]) : 0u;
+  }
+  float top = 0.f, sum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !(taken >> i & 1u)) {
+        const uint64_t kk = ((uint64_t)key[i] << 32) | (uint32_t)(kMaxExperts - 1 - e);
+        best = kk > best ? kk : best;
+      }
+    }
+    best = wave_max_u64(best);
+    const int e = kMaxExperts - 1 - (int)(best & 0xffffffffu);
+    const float v = from_ordered((uint32_t)(best >> 32));
+    if (j == 0) top = v;
+    sum += expf(v - top);
+    if ((e & 63) == lane) taken |= 1u << (e >> 6);
+    if (lane == 0) {
+      ids[(int64_t)t * k + j] = e;
+      wts[(int64_t)t * k + j] = v;
+    }
+  }
+  if (lane == 0) {
+    const float inv = 1.0f / sum;
+    for (int j = 0; j < k; ++j) wts[(int64_t)t * k + j] = expf(wts[(int64_t)t * k + j] - top) * inv;
+  }
+}
+
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                       hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  k_topk<<<(T + 3) / 4, 256, 0, stream>>>(logits, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+// Block = one wave of 64 tokens.  mask[e] bit l = token (64*blk + l) chose local expert e.
+__global__ __launch_bounds__(64) void k_rank(const int32_t* __restrict__ ids, int T, int k, int off,
+                                             int L, int32_t* __restrict__ hist,
+                                             int32_t* __restrict__ rank) {
+  __shared__ unsigned long long mask[kMaxExperts];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < L; e += 64) mask[e] = 0ull;
+  __syncthreads();
+  const int t = blockIdx.x * 64 + lane;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[(int64_t)t * k + j] - off;
+      if (e >= 0 && e < L) atomicOr(&mask[e], 1ull << lane);
+    }
+  }
+  __syncthreads();
+  for (int e = lane; e < L; e += 64) hist[(int64_t)blockIdx.x * L + e] = __popcll(mask[e]);
+  if (t < T) {
+    const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[(int64_t)t * k + j] - off;
+      rank[(int64_t)t * k + j] = (e >= 0 && e < L) ? __popcll(mask[e] & below) : -1;
+    }
+  }
+}
+
+// One block of 1024 threads; thread e owns local expert e.
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int nblk, int L,
+                                               int32_t* __restrict__ offsets, Tile* __restrict__ tiles,
+                                               int32_t* __restrict__ num_tiles, int bm) {
+  __shared__ int32_t s_a[kMaxExperts];
+  __shared__ int32_t s_b[kMaxExperts];
+  const int e = threadIdx.x;
+  int32_t count = 0;
+  if (e < L) {
+    for (int b = 0; b < nblk; ++b) {
+      const int32_t h = hist[(int64_t)b * L + e];
+      hist[(int64_t)b * L + e] = count;
+      count += h;
+    }
+  }
+  const int32_t ntile = (e < L && bm > 0) ? (count + bm - 1) / bm : 0;
+  // inclusive Hillis-Steele scans of count and ntile over the block
+  s_a[e] = e < L ? count : 0;
+  s_b[e] = ntile;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int32_t a = e >= d ? s_a[e - d] : 0;
+    const int32_t b = e >= d ? s_b[e - d] : 0;
+    __syncthreads();
+    s_a[e] += a;
+    s_b[e] += b;
+    __syncthreads();
+  }
+  const int32_t start = s_a[e] - (e < L ? count : 0);
+  const int32_t tstart = s_b[e] - ntile;
+  if (e < L) {
+    offsets[e] = start;
+    if (e == L - 1) offsets[L] = s_a[e];
+    for (int b = 0; b < nblk; ++b) hist[(int64_t)b * L + e] += start;
+    for (int i = 0; i < ntile; ++i) {
+      const int32_t r0 = i * bm;
+      Tile tl;
+      tl.expert = e;
+      tl.p0 = start + r0;
+      tl.rows = min(bm, count - r0);
+      tl.pad = 0;
+      tiles[tstart + i] = tl;
+    }
+  }
+  if (e == 0 && bm > 0) *num_tiles = s_b[1023];
+}
+
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, int T, int k,
+                                                 int off, int L, const int32_t* __restrict__ base,
+                                                 const int32_t* __restrict__ rank,
+                                                 int32_t* __restrict__ sorted_assign) {
+  const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (a >= (int64_t)T * k) return;
+  const int e = ids[a] - off;
+  if (e < 0 || e >= L) return;
+  const int64_t blk = (a / k) / 64;
+  sorted_assign[base[blk * L + e] + rank[a]] = (int32_t)a;
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int k, int off, int L, int32_t* hist,
+                          int32_t* rank, int32_t* offsets, int32_t* sorted_assign, Tile* tiles,
+                          int32_t* num_tiles, int bm, hipStream_t stream) {
+  const int nblk = (T + 63) / 64;
+  if (nblk > 0) k_rank<<<nblk, 64, 0, stream>>>(ids, T, k, off, L, hist, rank);
+  k_scan<<<1, 1024, 0, stream>>>(hist, nblk, L, offsets, tiles, num_tiles, tiles ? bm : 0);
+  const int64_t A = (int64_t)T * k;
+  if (A > 0) k_scatter<<<(A + 255) / 256, 256, 0, stream>>>(ids, T, k, off, L, hist, rank, sorted_assign);
+  return hipGetLastError();
+}
+
+}  // namespace moe_mx
