@@ -244,6 +244,11 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     if (r != hipSuccess && e == hipSuccess) e = r;
     return r == hipSuccess;
   };
+  // optional instrumentation: event i marks the start of stage i
+  auto mark = [&](int stage) {
+    return t->stage_events == nullptr || hipEventRecord(t->stage_events[stage], stream) == hipSuccess;
+  };
+  if (!mark(MOE_STAGE_ROUTE)) return MOE_ERR_HIP;
 
   // fp32 accumulator <- 0 (a fill kernel, so the sequence stays graph-capturable)
   const int64_t n4 = (int64_t)T * H / 4;
@@ -268,6 +273,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     wts = w_w;
   }
   // 2. permutation by local expert + tile list
+  if (!mark(MOE_STAGE_PERMUTE)) return MOE_ERR_HIP;
   int32_t* sorted = (int32_t*)(ws + f.sorted);
   Tile* tiles = (Tile*)(ws + f.tiles);
   int32_t* ntiles = (int32_t*)(ws + f.ntiles);
@@ -275,6 +281,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
                          (int32_t*)(ws + f.offsets), sorted, tiles, ntiles, kStreamRows, stream)))
     return MOE_ERR_HIP;
   // 3. MXFP8 activations
+  if (!mark(MOE_STAGE_QUANT_X)) return MOE_ERR_HIP;
   const uint8_t* xq = (const uint8_t*)(ws + f.xq);
   const uint8_t* xs = (const uint8_t*)(ws + f.xs);
   if (mx && !ok(launch_quantize(t->x, MOE_SRC_BF16, T, H, H, MX_E4M3, (uint8_t*)xq, (uint8_t*)xs, stream)))
@@ -283,6 +290,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   const int64_t bytes_h = (int64_t)H * wbits(p->w_fmt) / 8;
   const int64_t bytes_i = (int64_t)I * wbits(p->w_fmt) / 8;
   // 4-5. FC1 + SiLU(gate)*up (+ MXFP8 requantization)
+  if (!mark(MOE_STAGE_FC1)) return MOE_ERR_HIP;
   FcArgs a1 = {};
   a1.tiles = tiles;
   a1.num_tiles = ntiles;
@@ -304,6 +312,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.out_scale = (uint8_t*)(ws + f.hsc);
   if (!ok(launch_fc_stream(a1, true, mx, wf, stream))) return MOE_ERR_HIP;
   // 6-7. FC2 + weighted combine into the fp32 accumulator
+  if (!mark(MOE_STAGE_FC2)) return MOE_ERR_HIP;
   FcArgs a2 = a1;
   a2.a = ws + f.h;
   a2.a_scale = (const uint8_t*)(ws + f.hsc);
@@ -318,6 +327,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a2.y_acc = yacc;
   if (!ok(launch_fc_stream(a2, false, mx, wf, stream))) return MOE_ERR_HIP;
   // shared expert: a dense expert over all T tokens with its own weight
+  if (!mark(MOE_STAGE_SHARED)) return MOE_ERR_HIP;
   if (Is > 0) {
     const int64_t bytes_is = (int64_t)Is * wbits(p->w_fmt) / 8;
     FcArgs s1 = a1;
@@ -346,7 +356,9 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     if (!ok(launch_fc_stream(s2, false, mx, wf, stream))) return MOE_ERR_HIP;
   }
   // 8. y = bf16(accumulator)
+  if (!mark(MOE_STAGE_FINALIZE)) return MOE_ERR_HIP;
   k_finalize<<<grid_for(n4, 256, 8192), 256, 0, stream>>>((const float4*)yacc, (uint2*)t->y, n4);
   if (!ok(hipGetLastError())) return MOE_ERR_HIP;
+  if (!mark(MOE_NUM_STAGES)) return MOE_ERR_HIP;
   return MOE_OK;
 }

@@ -39,10 +39,14 @@ class MoeProblem(ctypes.Structure):
                 ("local_expert_offset", ctypes.c_int32), ("local_num_experts", ctypes.c_int32)]
 
 
+MOE_NUM_STAGES = 7
+STAGES = ("route", "permute", "quant_x", "fc1", "fc2", "shared", "finalize")
+
+
 class MoeTensors(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "router_logits", "topk_ids_in", "topk_w_in", "w1", "w1_scale", "w2", "w2_scale",
-        "ws1", "ws1_scale", "ws2", "ws2_scale", "y", "topk_ids_out", "topk_w_out")]
+        "ws1", "ws1_scale", "ws2", "ws2_scale", "y", "topk_ids_out", "topk_w_out", "stage_events")]
 
 
 _lib = None
@@ -173,8 +177,11 @@ def moe_fused_workspace_bytes(problem: MoeProblem) -> int:
 
 def moe_fused(problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, router_logits=None,
               topk_ids_in=None, topk_w_in=None, y=None, workspace=None, topk_ids_out=None,
-              topk_w_out=None, stream=None):
-    """Run the whole layer; returns y [T, H] bf16."""
+              topk_w_out=None, stream=None, stage_events=None):
+    """Run the whole layer; returns y [T, H] bf16.
+
+    stage_events: optional ctypes array of MOE_NUM_STAGES + 1 hipEvent_t
+    handles (see HipEvents) recorded at the stage boundaries."""
     _dev(x, router_logits, topk_ids_in, topk_w_in, weights.w1, weights.w2)
     if y is None:
         y = torch.empty((problem.T, problem.H), dtype=torch.bfloat16, device=x.device)
@@ -184,7 +191,47 @@ def moe_fused(problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, router_
     t = MoeTensors(*(None if v is None else v.data_ptr() for v in (
         x, router_logits, topk_ids_in, topk_w_in, weights.w1, weights.w1_scale, weights.w2,
         weights.w2_scale, weights.ws1, weights.ws1_scale, weights.ws2, weights.ws2_scale, y,
-        topk_ids_out, topk_w_out)))
+        topk_ids_out, topk_w_out)), None)
+    if stage_events is not None:
+        t.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
     _check(lib().moe_fused(ctypes.byref(problem), ctypes.byref(t), _ptr(workspace), workspace.numel(),
                            _stream(stream)), "moe_fused")
     return y
+
+
+# ------------------------------------------------------------ HIP events --
+
+class HipEvents:
+    """A set of HIP events created with the HIP runtime that torch loaded (the
+    library links the same one), for timing work on a given stream."""
+
+    def __init__(self, n: int):
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                   ctypes.c_void_p]
+        self.handles = (ctypes.c_void_p * n)()
+        for i in range(n):
+            r = self._hip.hipEventCreate(ctypes.byref(self.handles, i * ctypes.sizeof(ctypes.c_void_p)))
+            if r != 0:
+                raise RuntimeError(f"hipEventCreate failed ({r})")
+
+    def record(self, i: int, stream=None):
+        r = self._hip.hipEventRecord(ctypes.c_void_p(self.handles[i]), _stream(stream))
+        if r != 0:
+            raise RuntimeError(f"hipEventRecord failed ({r})")
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        r = self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.handles[i]),
+                                          ctypes.c_void_p(self.handles[j]))
+        if r != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({r})")
+        return ms.value
+
+    def __del__(self):
+        try:
+            for h in self.handles:
+                if h:
+                    self._hip.hipEventDestroy(ctypes.c_void_p(h))
+        except Exception:
+            pass

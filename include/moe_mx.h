@@ -156,7 +156,24 @@ typedef struct {
   void* y;                       /* [T, H] bf16 out, overwritten                         */
   int32_t* topk_ids_out;         /* [T, k] optional: routing ids used                    */
   float* topk_w_out;             /* [T, k] optional: routing weights used                */
+  const hipEvent_t* stage_events;/* optional [MOE_NUM_STAGES + 1] caller-created events:  */
+                                 /* event i is recorded on `stream` when stage i starts, */
+                                 /* the last one after the final stage (NULL: none)      */
 } moe_tensors_t;
+
+/* Stages of moe_fused, in launch order, for stage_events.  A stage that a
+ * problem does not need (x quantization with bf16 activations, the shared
+ * expert without one) still records its event and takes no time. */
+enum {
+  MOE_STAGE_ROUTE = 0,     /* zero the fp32 accumulator; top-k routing (or copy of given top-k) */
+  MOE_STAGE_PERMUTE = 1,   /* histogram, scan, permutation and tile list                        */
+  MOE_STAGE_QUANT_X = 2,   /* MXFP8 quantization of x                                           */
+  MOE_STAGE_FC1 = 3,       /* FC1 grouped GEMM + SiLU(gate)*up (+ MXFP8 requantization)         */
+  MOE_STAGE_FC2 = 4,       /* FC2 grouped GEMM + routing-weighted combine                       */
+  MOE_STAGE_SHARED = 5,    /* shared expert FC1 + FC2                                           */
+  MOE_STAGE_FINALIZE = 6,  /* fp32 accumulator -> bf16 y                                        */
+  MOE_NUM_STAGES = 7
+};
 
 /*
  * moe_fused -- the whole layer (steps 1-7 above) on `stream`.
