@@ -44,4 +44,13 @@ constexpr int kStreamRows = 16;
 
 hipError_t launch_fc_stream(const FcArgs& p, bool fc1, bool mx_act, int wfmt, hipStream_t st);
 
+// Tiled variant (MXFP8 activations): M-tiles of up to kTiledRows rows, N-blocks
+// of 64 h columns (FC1: nchunks = I / 64) or 128 output columns (FC2:
+// nchunks = H / 128); `grid` persistent workgroups (rounded down to a multiple
+// of 8, at least 8).
+constexpr int kTiledRows = 256;
+constexpr int kTiledColsFc1 = 64;
+constexpr int kTiledColsFc2 = 128;
+hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int grid, hipStream_t st);
+
 }  // namespace moe_mx

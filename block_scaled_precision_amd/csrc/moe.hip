@@ -38,6 +38,21 @@ moe_status_t check_arch() {
   return ok ? MOE_OK : MOE_ERR_ARCH;
 }
 
+// Compute units of the current device (cached per device), for persistent grids.
+static int device_cus() {
+  static std::atomic<int> cache[256];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 256) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 256) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // ------------------------------------------------------- small kernels ----
 
 __global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, int64_t n4) {
@@ -79,9 +94,16 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static int wbits(mx_elem_t f) { return f == MX_E2M1 ? 4 : (f == MX_E3M2 ? 6 : 8); }
 
+// Routed GEMMs run tiled (LDS-staged, M-tiles of up to kTiledRows rows) when the
+// activations are MXFP8 and the local experts average at least this many rows;
+// otherwise the stream kernels (16-row tiles, weights straight from HBM) run.
+constexpr int kTiledMinRowsPerExpert = 16;
+
 struct FusedPlan {
   int L, off;
   int64_t A;
+  bool tiled, shared_tiled;
+  int bm;
   int nblk, max_tiles;
   size_t ids, w, rank, hist, offsets, sorted, tiles, ntiles, xq, xs, h, hsc, hs, hssc, yacc, total;
 };
@@ -92,7 +114,11 @@ static FusedPlan plan(const moe_problem_t& p) {
   f.L = p.local_num_experts == 0 ? p.E : p.local_num_experts;
   f.A = (int64_t)p.T * p.k;
   f.nblk = (p.T + kTokensPerRouteBlock - 1) / kTokensPerRouteBlock;
-  f.max_tiles = (int)(f.A / kStreamRows + (f.A < f.L ? f.A : f.L));
+  const bool mxa = p.act == MOE_ACT_MXFP8;
+  f.tiled = mxa && f.L > 0 && f.A >= (int64_t)kTiledMinRowsPerExpert * f.L;
+  f.shared_tiled = mxa && p.T >= kTiledMinRowsPerExpert;
+  f.bm = f.tiled ? kTiledRows : kStreamRows;
+  f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t r = o;
@@ -278,7 +304,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   Tile* tiles = (Tile*)(ws + f.tiles);
   int32_t* ntiles = (int32_t*)(ws + f.ntiles);
   if (!ok(launch_permute(ids, T, k, f.off, f.L, (int32_t*)(ws + f.hist), (int32_t*)(ws + f.rank),
-                         (int32_t*)(ws + f.offsets), sorted, tiles, ntiles, kStreamRows, stream)))
+                         (int32_t*)(ws + f.offsets), sorted, tiles, ntiles, f.bm, stream)))
     return MOE_ERR_HIP;
   // 3. MXFP8 activations
   if (!mark(MOE_STAGE_QUANT_X)) return MOE_ERR_HIP;
@@ -307,10 +333,14 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.ws_estride = 2 * (int64_t)I * (H / 32);
   a1.K = H;
   a1.N = I;
-  a1.nchunks = I / kStreamColsFc1;
+  a1.nchunks = I / (f.tiled ? kTiledColsFc1 : kStreamColsFc1);
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
-  if (!ok(launch_fc_stream(a1, true, mx, wf, stream))) return MOE_ERR_HIP;
+  const int cus = device_cus();
+  auto launch_fc = [&](const FcArgs& a, bool fc1, bool tiled) {
+    return tiled ? launch_fc_tiled(a, fc1, wf, cus, stream) : launch_fc_stream(a, fc1, mx, wf, stream);
+  };
+  if (!ok(launch_fc(a1, true, f.tiled))) return MOE_ERR_HIP;
   // 6-7. FC2 + weighted combine into the fp32 accumulator
   if (!mark(MOE_STAGE_FC2)) return MOE_ERR_HIP;
   FcArgs a2 = a1;
@@ -322,10 +352,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a2.ws_estride = (int64_t)H * (I / 32);
   a2.K = I;
   a2.N = H;
-  a2.nchunks = H / kStreamColsFc2;
+  a2.nchunks = H / (f.tiled ? kTiledColsFc2 : kStreamColsFc2);
   a2.out = nullptr;
   a2.y_acc = yacc;
-  if (!ok(launch_fc_stream(a2, false, mx, wf, stream))) return MOE_ERR_HIP;
+  if (!ok(launch_fc(a2, false, f.tiled))) return MOE_ERR_HIP;
   // shared expert: a dense expert over all T tokens with its own weight
   if (!mark(MOE_STAGE_SHARED)) return MOE_ERR_HIP;
   if (Is > 0) {
@@ -337,10 +367,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s1.w_estride = 0;
     s1.ws_estride = 0;
     s1.N = Is;
-    s1.nchunks = Is / kStreamColsFc1;
+    s1.nchunks = Is / (f.shared_tiled ? kTiledColsFc1 : kStreamColsFc1);
     s1.out = ws + f.hs;
     s1.out_scale = (uint8_t*)(ws + f.hssc);
-    if (!ok(launch_fc_stream(s1, true, mx, wf, stream))) return MOE_ERR_HIP;
+    if (!ok(launch_fc(s1, true, f.shared_tiled))) return MOE_ERR_HIP;
     FcArgs s2 = a2;
     s2.dense_rows = T;
     s2.dense_weight = p->shared_weight;
@@ -351,9 +381,9 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s2.w_estride = 0;
     s2.ws_estride = 0;
     s2.K = Is;
-    s2.nchunks = H / kStreamColsFc2;
+    s2.nchunks = H / (f.shared_tiled ? kTiledColsFc2 : kStreamColsFc2);
     (void)bytes_is;
-    if (!ok(launch_fc_stream(s2, false, mx, wf, stream))) return MOE_ERR_HIP;
+    if (!ok(launch_fc(s2, false, f.shared_tiled))) return MOE_ERR_HIP;
   }
   // 8. y = bf16(accumulator)
   if (!mark(MOE_STAGE_FINALIZE)) return MOE_ERR_HIP;
