@@ -18,6 +18,7 @@ struct FcArgs {
   const int32_t* sorted_assign;
   int k;
   const float* topk_w;  // FC2 routed: weight of assignment a
+  const float* sorted_w;  // routed: weight of permuted row p (= topk_w[sorted_assign[p]])
   float dense_weight;   // FC2 dense: weight of every row
   // A operand: FC1 -> x rows (bf16 [T, K] or E4M3 codes [T, K] + scales [T, K/32]),
   //            FC2 -> h rows in permuted order (bf16 [P, K] or codes + scales)
@@ -34,7 +35,8 @@ struct FcArgs {
   // outputs
   void* out;           // FC1: h (bf16 [P, I] or E4M3 codes [P, I])
   uint8_t* out_scale;  // FC1 MX: h scales [P, I/32]
-  float* y_acc;        // FC2: fp32 [T, H] accumulator
+  float* obuf;         // FC2: fp32 rows [A, N] (routed: row = assignment a, holding
+                       // w(a) * o; dense: row = token, holding dense_weight * o)
 };
 
 // Columns of N covered by one wave of the stream kernels.
@@ -47,10 +49,11 @@ hipError_t launch_fc_stream(const FcArgs& p, bool fc1, bool mx_act, int wfmt, hi
 // Tiled variant (MXFP8 activations): M-tiles of up to kTiledRows rows, N-blocks
 // of 64 h columns (FC1: nchunks = I / 64) or 128 output columns (FC2:
 // nchunks = H / 128); `grid` persistent workgroups (rounded down to a multiple
-// of 8, at least 8).
+// of 8, at least 8).  Requires K >= kTiledMinK.
 constexpr int kTiledRows = 256;
 constexpr int kTiledColsFc1 = 64;
 constexpr int kTiledColsFc2 = 128;
+constexpr int kTiledMinK = 256;
 hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int grid, hipStream_t st);
 
 }  // namespace moe_mx

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
-// FC2: y_acc[token(p), n] += w(p) * (A W2^T)[p, n] for the wave's 64 columns n;
+// FC2: obuf[a(p), n] = w(p) * (A W2^T)[p, n] for the wave's 64 columns n;
 // rows of A are rows of h in permuted order.
 template <bool MXA, int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_fc2_stream(FcArgs p) {
@@ -267,19 +267,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     const int row = 4 * g + i;
     if (row >= t.rows) continue;
     const int prow = t.p0 + row;
-    int tok;
+    int64_t orow;
     float w;
     if (p.dense_rows > 0) {
-      tok = prow;
+      orow = prow;
       w = p.dense_weight;
     } else {
       const int a = p.sorted_assign[prow];
-      tok = a / p.k;
+      orow = a;
       w = p.topk_w[a];
     }
-    float* y = p.y_acc + (int64_t)tok * H + col0 + r;
+    float* o = p.obuf + orow * H + col0 + r;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) unsafeAtomicAdd(y + 16 * n, w * acc[n][i]);
+    for (int n = 0; n < NB; ++n) o[16 * n] = w * acc[n][i];
   }
 }
 

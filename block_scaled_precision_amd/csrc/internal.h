@@ -34,10 +34,11 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 
 // Permutation of the T*k assignments over local experts [off, off+L):
 // per-block histograms `hist` [nblk, L] (turned into write bases in place),
-// ranks [T*k], counts-derived offsets [L+1], sorted_assign, and, if tiles is
-// non-null, the GEMM tile list for M-tiles of `bm` rows with its count.
-hipError_t launch_permute(const int32_t* ids, int T, int k, int off, int L, int32_t* hist,
-                          int32_t* rank, int32_t* offsets, int32_t* sorted_assign, Tile* tiles,
+// ranks [T*k], counts-derived offsets [L+1], sorted_assign, if sorted_w is
+// non-null the routing weights w in the same order, and, if tiles is non-null,
+// the GEMM tile list for M-tiles of `bm` rows with its count.
+hipError_t launch_permute(const int32_t* ids, const float* w, int T, int k, int off, int L, int32_t* hist,
+                          int32_t* rank, int32_t* offsets, int32_t* sorted_assign, float* sorted_w, Tile* tiles,
                           int32_t* num_tiles, int bm, hipStream_t stream);
 
 }  // namespace moe_mx

@@ -55,20 +55,32 @@ static int device_cus() {
 
 // ------------------------------------------------------- small kernels ----
 
-__global__ __launch_bounds__(256) void k_fill_zero(float4* __restrict__ p, int64_t n4) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
-    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-// y (bf16) = round-half-to-even of the fp32 accumulator
-__global__ __launch_bounds__(256) void k_finalize(const float4* __restrict__ acc, uint2* __restrict__ y,
-                                                  int64_t n4) {
+// Unpermute-combine (TokenSpeed SiTU page, "Supported contract": the layer
+// output is the routing-weighted sum over the selected experts; mxfp6-sm120
+// page, "Routed MoE": routed/shared reduction).  obuf row t*k + j holds
+// w[t,j] * FC2 output of assignment (t, j) in fp32; sbuf row t the weighted
+// shared-expert output (or nullptr).  y[t] = bf16 RNE of the sum over the
+// assignments whose expert lies in the local range [off, off + L) (rows of
+// other experts were never written), added in slot order, plus sbuf[t].
+__global__ __launch_bounds__(256) void k_combine(const float4* __restrict__ obuf, const float4* __restrict__ sbuf,
+                                                 const int32_t* __restrict__ ids, int k, int off, int L,
+                                                 int H4, int64_t n4, uint2* __restrict__ y) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const float4 v = acc[i];
-    const uint32_t lo = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+    const int64_t t = i / H4;
+    const int64_t c = i - t * H4;
+    float4 s = sbuf ? sbuf[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[t * k + j] - off;
+      if (e < 0 || e >= L) continue;
+      const float4 v = obuf[(t * k + j) * H4 + c];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(s.x) | ((uint32_t)f32_to_bf16_rne(s.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(s.z) | ((uint32_t)f32_to_bf16_rne(s.w) << 16);
     y[i] = make_uint2(lo, hi);
   }
 }
@@ -105,7 +117,7 @@ struct FusedPlan {
   bool tiled, shared_tiled;
   int bm;
   int nblk, max_tiles;
-  size_t ids, w, rank, hist, offsets, sorted, tiles, ntiles, xq, xs, h, hsc, hs, hssc, yacc, total;
+  size_t ids, w, rank, hist, offsets, sorted, sorted_w, tiles, ntiles, xq, xs, h, hsc, hs, hssc, obuf, sbuf, total;
 };
 
 static FusedPlan plan(const moe_problem_t& p) {
@@ -115,8 +127,9 @@ static FusedPlan plan(const moe_problem_t& p) {
   f.A = (int64_t)p.T * p.k;
   f.nblk = (p.T + kTokensPerRouteBlock - 1) / kTokensPerRouteBlock;
   const bool mxa = p.act == MOE_ACT_MXFP8;
-  f.tiled = mxa && f.L > 0 && f.A >= (int64_t)kTiledMinRowsPerExpert * f.L;
-  f.shared_tiled = mxa && p.T >= kTiledMinRowsPerExpert;
+  f.tiled = mxa && f.L > 0 && f.A >= (int64_t)kTiledMinRowsPerExpert * f.L && p.H >= kTiledMinK &&
+            p.I >= kTiledMinK;
+  f.shared_tiled = mxa && p.T >= kTiledMinRowsPerExpert && p.H >= kTiledMinK && p.I_shared >= kTiledMinK;
   f.bm = f.tiled ? kTiledRows : kStreamRows;
   f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
@@ -133,6 +146,7 @@ static FusedPlan plan(const moe_problem_t& p) {
   f.hist = take((size_t)f.nblk * f.L * 4);
   f.offsets = take((size_t)(f.L + 1) * 4);
   f.sorted = take(f.A * 4);
+  f.sorted_w = take(f.A * 4);
   f.tiles = take((size_t)f.max_tiles * sizeof(Tile));
   f.ntiles = take(4);
   f.xq = mx ? take(T * H) : 0;
@@ -141,7 +155,8 @@ static FusedPlan plan(const moe_problem_t& p) {
   f.hsc = mx ? take(f.A * I / 32) : 0;
   f.hs = Is ? take(T * Is * (mx ? 1 : 2)) : 0;
   f.hssc = (Is && mx) ? take(T * Is / 32) : 0;
-  f.yacc = take(T * H * 4);
+  f.obuf = take(f.A * H * 4);
+  f.sbuf = Is ? take(T * H * 4) : 0;
   f.total = o;
   return f;
 }
@@ -238,7 +253,8 @@ extern "C" moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int
   int32_t* hist = (int32_t*)ws;
   int32_t* rank = (int32_t*)(ws + align_up(nblk * E * 4, 256));
   if (launch_topk(logits, T, E, k, topk_ids, topk_w, stream) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_permute(topk_ids, T, k, 0, E, hist, rank, expert_offsets, sorted_assign, nullptr, nullptr, 0,
+  if (launch_permute(topk_ids, nullptr, T, k, 0, E, hist, rank, expert_offsets, sorted_assign, nullptr, nullptr,
+                     nullptr, 0,
                      stream) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
@@ -264,7 +280,8 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   const bool mx = p->act == MOE_ACT_MXFP8;
   const int wf = p->w_fmt == MX_E2M1 ? 1 : 2;
   const int T = p->T, H = p->H, I = p->I, k = p->k, Is = p->I_shared;
-  float* yacc = (float*)(ws + f.yacc);
+  float* obuf = (float*)(ws + f.obuf);
+  float* sbuf = Is ? (float*)(ws + f.sbuf) : nullptr;
   hipError_t e = hipSuccess;
   auto ok = [&](hipError_t r) {
     if (r != hipSuccess && e == hipSuccess) e = r;
@@ -275,11 +292,6 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     return t->stage_events == nullptr || hipEventRecord(t->stage_events[stage], stream) == hipSuccess;
   };
   if (!mark(MOE_STAGE_ROUTE)) return MOE_ERR_HIP;
-
-  // fp32 accumulator <- 0 (a fill kernel, so the sequence stays graph-capturable)
-  const int64_t n4 = (int64_t)T * H / 4;
-  k_fill_zero<<<grid_for(n4, 256, 8192), 256, 0, stream>>>((float4*)yacc, n4);
-  if (!ok(hipGetLastError())) return MOE_ERR_HIP;
 
   // 1. routing
   const int32_t* ids;
@@ -303,8 +315,9 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   int32_t* sorted = (int32_t*)(ws + f.sorted);
   Tile* tiles = (Tile*)(ws + f.tiles);
   int32_t* ntiles = (int32_t*)(ws + f.ntiles);
-  if (!ok(launch_permute(ids, T, k, f.off, f.L, (int32_t*)(ws + f.hist), (int32_t*)(ws + f.rank),
-                         (int32_t*)(ws + f.offsets), sorted, tiles, ntiles, f.bm, stream)))
+  float* sorted_w = (float*)(ws + f.sorted_w);
+  if (!ok(launch_permute(ids, wts, T, k, f.off, f.L, (int32_t*)(ws + f.hist), (int32_t*)(ws + f.rank),
+                         (int32_t*)(ws + f.offsets), sorted, sorted_w, tiles, ntiles, f.bm, stream)))
     return MOE_ERR_HIP;
   // 3. MXFP8 activations
   if (!mark(MOE_STAGE_QUANT_X)) return MOE_ERR_HIP;
@@ -325,6 +338,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.sorted_assign = sorted;
   a1.k = k;
   a1.topk_w = wts;
+  a1.sorted_w = sorted_w;
   a1.a = mx ? (const void*)xq : t->x;
   a1.a_scale = xs;
   a1.w = t->w1;
@@ -354,7 +368,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a2.N = H;
   a2.nchunks = H / (f.tiled ? kTiledColsFc2 : kStreamColsFc2);
   a2.out = nullptr;
-  a2.y_acc = yacc;
+  a2.obuf = obuf;
   if (!ok(launch_fc(a2, false, f.tiled))) return MOE_ERR_HIP;
   // shared expert: a dense expert over all T tokens with its own weight
   if (!mark(MOE_STAGE_SHARED)) return MOE_ERR_HIP;
@@ -382,12 +396,15 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s2.ws_estride = 0;
     s2.K = Is;
     s2.nchunks = H / (f.shared_tiled ? kTiledColsFc2 : kStreamColsFc2);
+    s2.obuf = sbuf;
     (void)bytes_is;
     if (!ok(launch_fc(s2, false, f.shared_tiled))) return MOE_ERR_HIP;
   }
   // 8. y = bf16(accumulator)
   if (!mark(MOE_STAGE_FINALIZE)) return MOE_ERR_HIP;
-  k_finalize<<<grid_for(n4, 256, 8192), 256, 0, stream>>>((const float4*)yacc, (uint2*)t->y, n4);
+  const int64_t n4 = (int64_t)T * H / 4;
+  k_combine<<<grid_for(n4, 256, 16384), 256, 0, stream>>>((const float4*)obuf, (const float4*)sbuf, ids, k, f.off,
+                                                          f.L, H / 4, n4, (uint2*)t->y);
   if (!ok(hipGetLastError())) return MOE_ERR_HIP;
   if (!mark(MOE_NUM_STAGES)) return MOE_ERR_HIP;
   return MOE_OK;

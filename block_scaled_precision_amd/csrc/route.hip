@@ -167,26 +167,31 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   if (e == 0 && bm > 0) *num_tiles = s_b[1023];
 }
 
-__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, int T, int k,
-                                                 int off, int L, const int32_t* __restrict__ base,
+// sorted_assign[pos] = a and, if requested, sorted_w[pos] = w[a] (the routing
+// weight of the assignment, so that consumers of permuted rows read it directly)
+__global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                 int T, int k, int off, int L, const int32_t* __restrict__ base,
                                                  const int32_t* __restrict__ rank,
-                                                 int32_t* __restrict__ sorted_assign) {
+                                                 int32_t* __restrict__ sorted_assign, float* __restrict__ sorted_w) {
   const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (a >= (int64_t)T * k) return;
   const int e = ids[a] - off;
   if (e < 0 || e >= L) return;
   const int64_t blk = (a / k) / 64;
-  sorted_assign[base[blk * L + e] + rank[a]] = (int32_t)a;
+  const int32_t pos = base[blk * L + e] + rank[a];
+  sorted_assign[pos] = (int32_t)a;
+  if (sorted_w) sorted_w[pos] = w[a];
 }
 
-hipError_t launch_permute(const int32_t* ids, int T, int k, int off, int L, int32_t* hist,
-                          int32_t* rank, int32_t* offsets, int32_t* sorted_assign, Tile* tiles,
+hipError_t launch_permute(const int32_t* ids, const float* w, int T, int k, int off, int L, int32_t* hist,
+                          int32_t* rank, int32_t* offsets, int32_t* sorted_assign, float* sorted_w, Tile* tiles,
                           int32_t* num_tiles, int bm, hipStream_t stream) {
   const int nblk = (T + 63) / 64;
   if (nblk > 0) k_rank<<<nblk, 64, 0, stream>>>(ids, T, k, off, L, hist, rank);
   k_scan<<<1, 1024, 0, stream>>>(hist, nblk, L, offsets, tiles, num_tiles, tiles ? bm : 0);
   const int64_t A = (int64_t)T * k;
-  if (A > 0) k_scatter<<<(A + 255) / 256, 256, 0, stream>>>(ids, T, k, off, L, hist, rank, sorted_assign);
+  if (A > 0) k_scatter<<<(A + 255) / 256, 256, 0, stream>>>(ids, w, T, k, off, L, hist, rank, sorted_assign,
+                                                            sorted_w);
   return hipGetLastError();
 }
 

@@ -165,13 +165,13 @@ typedef struct {
  * problem does not need (x quantization with bf16 activations, the shared
  * expert without one) still records its event and takes no time. */
 enum {
-  MOE_STAGE_ROUTE = 0,     /* zero the fp32 accumulator; top-k routing (or copy of given top-k) */
+  MOE_STAGE_ROUTE = 0,     /* top-k routing (or copy of the given top-k)                        */
   MOE_STAGE_PERMUTE = 1,   /* histogram, scan, permutation and tile list                        */
   MOE_STAGE_QUANT_X = 2,   /* MXFP8 quantization of x                                           */
   MOE_STAGE_FC1 = 3,       /* FC1 grouped GEMM + SiLU(gate)*up (+ MXFP8 requantization)         */
-  MOE_STAGE_FC2 = 4,       /* FC2 grouped GEMM + routing-weighted combine                       */
+  MOE_STAGE_FC2 = 4,       /* FC2 grouped GEMM, routing weight applied, rows in token order     */
   MOE_STAGE_SHARED = 5,    /* shared expert FC1 + FC2                                           */
-  MOE_STAGE_FINALIZE = 6,  /* fp32 accumulator -> bf16 y                                        */
+  MOE_STAGE_FINALIZE = 6,  /* unpermute-combine: sum over slots (+ shared) -> bf16 y            */
   MOE_NUM_STAGES = 7
 };
 
@@ -182,8 +182,10 @@ enum {
  * [local_expert_offset, local_expert_offset + local_num_experts) contribute
  * and y is that shard's partial output (the caller sums shards); the shared
  * expert, if any, is added by every call.
- * Precision: FC products accumulate in fp32; y is one bf16 rounding of the
- * fp32 sum; the order of the fp32 additions across experts is not fixed.
+ * Precision: FC products accumulate in fp32; each expert's output row is
+ * scaled by its routing weight in fp32; y is one bf16 rounding of the fp32 sum
+ * of those rows taken in slot order j = 0..k-1, then the shared expert's
+ * (results are deterministic from run to run).
  * Workspace: at least moe_fused_workspace_bytes(p) bytes, 256-byte aligned.
  */
 size_t moe_fused_workspace_bytes(const moe_problem_t* p);

@@ -24,7 +24,7 @@ CASES = {
     "w4a8_single_token": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=1, H=256, I=128, E=8, k=2),
     # several 256-row M-tiles per expert with a ragged last tile
     "w4a8_multi_tile": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=700, H=256, I=256, E=4, k=2),
-    "w6a8_multi_tile_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=300, H=384, I=128, E=6, k=2,
+    "w6a8_multi_tile_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=300, H=384, I=256, E=2, k=2,
                                          I_shared=256),
 }
 
