@@ -9,24 +9,31 @@
 // expert, so an expert with <= 256 assignments streams its weights from HBM
 // exactly once; the N-block is 128 weight rows (FC1: 64 gate rows and the 64
 // matching up rows, i.e. 64 columns of h; FC2: 128 output columns).  The grid is
-// persistent: one workgroup of 8 waves per CU walks the items of its XCD (the
-// M-tiles x, x+8, ... of XCD x), so the N-blocks of one M-tile run together on
-// one XCD and its activation rows stay in that XCD's L2.
+// persistent: one workgroup per CU walks the items of its XCD (the M-tiles x,
+// x+8, ... of XCD x), so the N-blocks of one M-tile run together on one XCD and
+// its activation rows stay in that XCD's L2.  Items are consumed as one
+// continuous stream of (item, 128-K stage) steps with one workgroup barrier per
+// step.
 //
-// Data movement: a K-stage (128 values of K) of the A tile (gathered rows of
-// E4M3 codes, 128 B per row), of the B tile (packed weights, 64 B per row for
-// E2M1, 96 B for E3M2) and of their per-row scale words is copied straight
-// from global memory into LDS by global_load_lds (no register staging), into a
-// ring of three stage buffers: while stage s is multiplied, stages s+1 and s+2
-// are in flight.  The stream of (item, stage) steps is continuous across the
-// items of a workgroup, so the next item's first stages load during the
-// current item's last ones.  The copies are issued from inline assembly, so
-// the only waits on them are the explicit per-stage vmcnt waits below.
-//
-// Eight waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
-// are laid out 4 (M) x 2 (N): wave (wm, wn) owns the 32-row sub-blocks wm and
-// wm+4 of the tile (so a partly filled tile still spreads over all SIMDs) and
-// two 32-column MFMA tiles.
+// Waves have fixed roles (12 waves, three per SIMD):
+//  * waves 0-7 multiply: wave (wm, wn) = (w / 2, w % 2) owns the 32-row
+//    sub-blocks wm and wm + 4 of the tile (so a partly filled tile still
+//    spreads over all SIMDs) and two 32-column MFMA tiles, reads its operands
+//    from LDS and writes the item's results;
+//  * waves 8-9 copy the activation stage (gathered rows of E4M3 codes, 128 B per
+//    row and stage, plus the per-row scale words) into a ring of 3 LDS
+//    buffers, two stages ahead of the multiply;
+//  * waves 10-11 copy the weight stage (64 B per row and stage for E2M1, 96 B
+//    for E3M2, plus scale words) into a deeper ring (6 buffers for E2M1, 4 for
+//    E3M2) so that weights, which come from HBM, are requested 5 (3) stages
+//    ahead.
+// The copies are global_load_lds (global memory straight into LDS) issued from
+// inline assembly; each copy wave waits for its own stage with an explicit
+// vmcnt before the barrier.  Because a wave's memory counter drains in order,
+// the near (activation) and far (weight) streams live in different waves, and
+// the multiply waves issue no loads at all: the per-row metadata of an item
+// (source row, routing weight) is copied into LDS one item ahead by the
+// activation waves.
 //
 // MFMA operand layouts (v_mfma_scale_f32_32x32x64_f8f6f4, measured on the
 // device): lane l supplies row l%32 of its operand and the scale of (row l%32,
@@ -50,42 +57,65 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int TBM = kTiledRows;  // rows per M-tile (8 sub-blocks of 32)
 constexpr int TBN = 128;         // weight rows per work item
 constexpr int TBK = 128;         // K per stage
-constexpr int kWaves = 8;
+#ifndef MOE_TILED_MUL_WAVES
+#define MOE_TILED_MUL_WAVES 8
+#endif
+constexpr int kComputeWaves = MOE_TILED_MUL_WAVES;  // 4 or 8 multiply waves
+constexpr int kWaves = kComputeWaves + 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kWaveA = kComputeWaves;      // first activation-copy wave
+constexpr int kWaveB = kComputeWaves + 2;  // first weight-copy wave
+constexpr int kGroupsM = kComputeWaves / 2;  // multiply waves along M
+constexpr int kMaxSub = 8 / kGroupsM;        // 32-row sub-blocks per multiply wave
 
+// LDS layout: [A ring: 3 x (codes 32 KB + scale words 1 KB)]
+//             [B ring: NBS x (weights + scale words 512 B)]
+//             [row tables: 3 x (source row 1 KB + weight 1 KB)]
+constexpr int kAStages = 3;
+constexpr int A_CODES = TBM * TBK;
+constexpr int A_STAGE = A_CODES + TBM * 4;
 template <int WF> struct BLay {
-  static constexpr int ROW = WF == 1 ? 64 : 96;  // bytes of one weight row per stage
-  static constexpr int COPIES = TBN * ROW / 1024;  // 1-KB copies per stage: 8 (E2M1), 12 (E3M2)
-  static constexpr int PER_WAVE = (COPIES + kWaves - 1) / kWaves;  // 1 or 2
+  static constexpr int ROW = WF == 1 ? 64 : 96;    // bytes of one weight row per stage
+  static constexpr int CODES = TBN * ROW;
+  static constexpr int STAGE = CODES + TBN * 4;
+  static constexpr int COPIES = CODES / 1024;      // 1-KB copies per stage: 8 or 12
+  static constexpr int PER_WAVE = COPIES / 2;      // per weight-copy wave: 4 or 6
+  static constexpr int NBS = WF == 1 ? 6 : 4;      // ring depth
 };
-
+constexpr int TABLE = TBM * 8;
 template <int WF> struct Lds {
-  static constexpr int A = TBM * TBK;            // E4M3 codes
-  static constexpr int B = TBN * BLay<WF>::ROW;  // packed weights
-  static constexpr int SA = TBM * 4;             // 4 scale codes per row and stage
-  static constexpr int SB = TBN * 4;
-  static constexpr int STAGE = A + B + SA + SB;
+  static constexpr int A = 0;
+  static constexpr int B = kAStages * A_STAGE;
+  static constexpr int TBL = B + BLay<WF>::NBS * BLay<WF>::STAGE;
+  static constexpr int TOTAL = TBL + 3 * TABLE;
 };
 
-// Copies issued per wave and stage: 4 (A) + B + 1 scale copy.
-template <int WF> constexpr int copies_per_stage() { return 4 + BLay<WF>::PER_WAVE + 1; }
+// copies per copy-wave and stage
+constexpr int kACopies = 16 + 2;                                       // codes + scale words
+template <int WF> constexpr int b_copies() { return BLay<WF>::PER_WAVE + 1; }
 
 // s_waitcnt with vmcnt(n) and lgkmcnt(0) (gfx9 encoding; expcnt left at its maximum).
 template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
 // Asynchronous copies global -> LDS (global_load_lds): lane i of the wave writes
 // its `size` bytes at lds + size*i; `lds` is a wave-uniform LDS byte address.
 // M0 carries the LDS address; one wait state separates its write from the copy.
 __device__ __forceinline__ void lds_copy16(const uint8_t* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(src) : "memory");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
 }
-__device__ __forceinline__ void lds_copy4(const uint8_t* src, uint32_t lds) {
+__device__ __forceinline__ void lds_copy4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds), "v"(src) : "memory");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
+}
+
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
@@ -102,16 +132,37 @@ struct ItemGeom {
   int expert, p0, rows, nb;
 };
 
-__device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, int xcd, int j, int NB) {
+struct Sched {
+  int xcd, q, Q, NB, nk, my_items, total;
+};
+
+// Tile-list entry through the scalar cache: a scalar load counts on lgkmcnt,
+// not on the vector memory counter that tracks the copies in flight, so
+// reading the next item's geometry never waits for them.  The load and its
+// wait sit in one asm block.
+__device__ __forceinline__ Tile load_tile(const Tile* tiles, int ti) {
+  const Tile* ptr = tiles + __builtin_amdgcn_readfirstlane(ti);
+  int4 v;
+  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  Tile t;
+  t.expert = v.x;
+  t.p0 = v.y;
+  t.rows = v.z;
+  t.pad = v.w;
+  return t;
+}
+
+__device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, const Sched& sc, int li) {
+  const int j = sc.q + li * sc.Q;
+  const int ti = sc.xcd + 8 * (j / sc.NB);
   ItemGeom g;
-  const int ti = xcd + 8 * (j / NB);
-  g.nb = j % NB;
+  g.nb = j % sc.NB;
   if (p.dense_rows > 0) {
     g.expert = 0;
     g.p0 = TBM * ti;
     g.rows = min(TBM, p.dense_rows - TBM * ti);
   } else {
-    const Tile t = p.tiles[ti];
+    const Tile t = load_tile(p.tiles, ti);
     g.expert = t.expert;
     g.p0 = t.p0;
     g.rows = t.rows;
@@ -119,21 +170,14 @@ __device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, int xcd, int j, i
   return g;
 }
 
-// Per-thread source addresses of one item's copies at stage 0 (stage s adds a
-// fixed stride) and the wave-uniform LDS offsets they land at.
-template <int WF>
-struct LoadGeom {
-  const uint8_t* a[4];  // A: 16-B chunk of row 8*(4*wave + i) + lane/8
-  const uint8_t* b[BLay<WF>::PER_WAVE];
-  const uint8_t* sc;    // waves 0-3: A scale word of row 64*wave + lane;
-                        // waves 4-7: B scale word of row 64*(wave & 1) + lane
-};
-
-// row of the gathered activations that feeds tile row r (r < it.rows)
-template <bool FC1>
-__device__ __forceinline__ int64_t a_src_row(const FcArgs& p, int prow) {
-  if (!FC1 || p.dense_rows > 0) return prow;
-  return p.sorted_assign[prow] / p.k;
+// K stage copied at step ls of an item.  The N-blocks of one M-tile run at the
+// same time on one XCD and read the same activation rows; starting each at a
+// different K stage (rotated by its N-block index) means only the first to
+// reach a stage misses in L2 and the others hit, instead of all of them
+// waiting on the same miss.  The multiply is indifferent to the K order.
+__device__ __forceinline__ int k_stage(const Sched& sc, int nb, int ls) {
+  const int s = ls + nb * sc.nk / sc.NB;
+  return s < sc.nk ? s : s - sc.nk;
 }
 
 // weight row held at B-tile row jr
@@ -143,75 +187,17 @@ __device__ __forceinline__ int64_t w_row(const FcArgs& p, int nb, int jr) {
   return (int64_t)nb * TBN + jr;
 }
 
-template <int WF> __device__ __forceinline__ int b_copy(int wv, int i) {
-  // E3M2: waves 0-3 take copies wv and 8+wv, waves 4-7 repeat their first copy
-  // (the same bytes to the same place) so that every wave issues as many copies
-  if (WF == 1) return wv;
-  return i == 0 ? wv : (wv < 4 ? 8 + wv : wv);
-}
+// ------------------------------------------------------------ multiply ---
 
-template <bool FC1, int WF>
-__device__ __forceinline__ void setup_loads(const FcArgs& p, const ItemGeom& it, LoadGeom<WF>& lg) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int K = p.K;
-  // rows outside the tile copy the tile's last row (their results are never stored)
-  const int c = (lane & 7) ^ (lane >> 3);  // chunk that lands in this lane's LDS slot
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = min(8 * (4 * wv + i) + (lane >> 3), it.rows - 1);
-    lg.a[i] = (const uint8_t*)p.a + a_src_row<FC1>(p, it.p0 + r) * K + 16 * c;
-  }
-  const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride;
-  const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride;
-  const int64_t wrow = (int64_t)K * Fmt<WF>::BITS / 8;
-#pragma unroll
-  for (int i = 0; i < BLay<WF>::PER_WAVE; ++i) {
-    const int t = b_copy<WF>(wv, i);
-    int jr, ch;
-    if (WF == 1) {
-      jr = 16 * t + (lane >> 2);
-      ch = (lane & 3) ^ ((jr >> 1) & 3);
-    } else {
-      const int cc = 64 * t + lane;
-      jr = cc / 6;
-      ch = cc % 6;
-    }
-    lg.b[i] = wb + w_row<FC1>(p, it.nb, jr) * wrow + 16 * ch;
-  }
-  if (wv < 4) {
-    const int r = min(64 * wv + lane, it.rows - 1);
-    lg.sc = p.a_scale + a_src_row<FC1>(p, it.p0 + r) * (K / 32);
-  } else {
-    lg.sc = sb + w_row<FC1>(p, it.nb, 64 * (wv & 1) + lane) * (K / 32);
-  }
-}
-
-template <int WF>
-__device__ __forceinline__ void issue_stage(const LoadGeom<WF>& lg, int s, uint32_t buf) {
-  using L = Lds<WF>;
-  const int wv = threadIdx.x >> 6;
-  const int ao = s * TBK, bo = s * (TBK * Fmt<WF>::BITS / 8), so = 4 * s;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lds_copy16(lg.a[i] + ao, __builtin_amdgcn_readfirstlane(buf + 1024 * (4 * wv + i)));
-#pragma unroll
-  for (int i = 0; i < BLay<WF>::PER_WAVE; ++i)
-    lds_copy16(lg.b[i] + bo, __builtin_amdgcn_readfirstlane(buf + L::A + 1024 * b_copy<WF>(wv, i)));
-  const uint32_t so_lds = wv < 4 ? buf + L::A + L::B + 256 * wv : buf + L::A + L::B + L::SA + 256 * (wv & 1);
-  lds_copy4(lg.sc + so, __builtin_amdgcn_readfirstlane(so_lds));
-}
-
-// One 128-K stage for a wave holding NM (1 or 2) sub-blocks: sub-block
-// wm + 4m of the tile times the wave's two 32-column B tiles.
+// One 128-K stage for a wave holding NM (1 to kMaxSub) sub-blocks: sub-block
+// wm + kGroupsM*m of the tile times the wave's two 32-column B tiles.
 template <int WF, int NM>
-__device__ __forceinline__ void compute_stage(v16f (&acc)[2][2], const uint8_t* base, int wm, int brow0,
-                                              int brow1) {
-  using L = Lds<WF>;
+__device__ __forceinline__ void compute_stage(v16f (&acc)[kMaxSub][2], const uint8_t* as, const uint8_t* bs, int wm,
+                                              int brow0, int brow1) {
   using BL = BLay<WF>;
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
-  const uint8_t* As = base;
-  const uint8_t* Bs = base + L::A;
-  const uint32_t* SAs = (const uint32_t*)(base + L::A + L::B);
-  const uint32_t* SBs = (const uint32_t*)(base + L::A + L::B + L::SA);
+  const uint32_t* SAs = (const uint32_t*)(as + A_CODES);
+  const uint32_t* SBs = (const uint32_t*)(bs + BL::CODES);
   v8i bv[2][2];
   uint32_t bsw[2];
   v8i av[2][NM];
@@ -224,10 +210,10 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[2][2], const uint8_t* 
     for (int kk = 0; kk < 2; ++kk) {
       const int blk = 2 * kk + g;
       if (WF == 1) {
-        const uint4 v = *(const uint4*)(Bs + b4_off(jr, blk));
+        const uint4 v = *(const uint4*)(bs + b4_off(jr, blk));
         bv[kk][n] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
       } else {
-        const uint8_t* rp = Bs + jr * BL::ROW + 24 * blk;
+        const uint8_t* rp = bs + jr * BL::ROW + 24 * blk;
         if ((blk & 1) == 0) {
           const uint4 v = *(const uint4*)rp;
           const uint2 d = *(const uint2*)(rp + 16);
@@ -242,12 +228,12 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[2][2], const uint8_t* 
   }
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    const int r = 32 * (wm + 4 * m) + l32;
+    const int r = 32 * (wm + kGroupsM * m) + l32;
     asw[m] = SAs[r];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const uint4 lo = *(const uint4*)(As + a_off(r, 4 * kk + g));
-      const uint4 hi = *(const uint4*)(As + a_off(r, 4 * kk + 2 + g));
+      const uint4 lo = *(const uint4*)(as + a_off(r, 4 * kk + g));
+      const uint4 hi = *(const uint4*)(as + a_off(r, 4 * kk + 2 + g));
       av[kk][m] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   }
@@ -266,62 +252,54 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[2][2], const uint8_t* 
   }
 }
 
-}  // namespace
-
 template <bool FC1, int WF>
-__global__ __launch_bounds__(kThreads, 1) void k_fc_tiled(FcArgs p) {
+__device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
   using L = Lds<WF>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[3 * L::STAGE];
-  constexpr int D = copies_per_stage<WF>();
-
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  using BL = BLay<WF>;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // 8 waves: (wm, wn) = (w / 2, w % 2), so the two multiply waves of a SIMD
+  // (w and w + 4) hold sub-blocks {wm, wm + 4} and {wm + 2, wm + 6};
+  // 4 waves: (w % 2, w / 2)
+  const int wm = kComputeWaves == 8 ? wv >> 1 : wv & 1;
+  const int wn = kComputeWaves == 8 ? wv & 1 : wv >> 1;
   const int l32 = lane & 31, g = lane >> 5;
-  const int nk = p.K / TBK, NB = p.nchunks;
-  const int ntiles = p.dense_rows > 0 ? (p.dense_rows + TBM - 1) / TBM : *p.num_tiles;
-  const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3, Q = gridDim.x >> 3;
-  const int xt = ntiles > xcd ? (ntiles - xcd + 7) / 8 : 0;
-  const int nitems = xt * NB;
-  const int my_items = nitems > q ? (nitems - q + Q - 1) / Q : 0;
-  const int total = my_items * nk;  // (item, stage) steps of this workgroup
-  if (total == 0) return;
-  const uint32_t lds0 = lds_addr(smem);
+  const int brow0 = FC1 ? 32 * wn : 64 * wn;
+  const int brow1 = FC1 ? TBN / 2 + 32 * wn : 64 * wn + 32;
 
-  // load cursor: item li (j = q + li*Q), stage ls
-  int li = 0, ls = 0;
-  LoadGeom<WF> lg;
-  setup_loads<FC1, WF>(p, item_geom(p, xcd, q, NB), lg);
-  auto issue_next = [&](int bufi) {
-    issue_stage<WF>(lg, ls, lds0 + bufi * L::STAGE);
-    if (++ls == nk) {
-      ls = 0;
-      if (++li < my_items) setup_loads<FC1, WF>(p, item_geom(p, xcd, q + li * Q, NB), lg);
-    }
-  };
-  issue_next(0);
-  if (total > 1) issue_next(1);
-
-  // compute cursor
-  int ci = 0, cs = 0;
-  ItemGeom cit = item_geom(p, xcd, q, NB);
-  int nm = (wm < ((cit.rows + 31) >> 5)) + (wm + 4 < ((cit.rows + 31) >> 5));
-  v16f acc[2][2];
+  v16f acc[kMaxSub][2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < kMaxSub; ++m)
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.f;
 
-  // B-tile rows of this wave's two column tiles
-  const int brow0 = FC1 ? 32 * wn : 64 * wn;
-  const int brow1 = FC1 ? TBN / 2 + 32 * wn : 64 * wn + 32;
+  // sub-blocks of this wave in a tile of `rows` rows
+  auto wave_subs = [&](int rows) { return max(0, (((rows + 31) >> 5) - wm + kGroupsM - 1) / kGroupsM); };
+  int ci = 0, cs = 0;
+  ItemGeom it = item_geom(p, sc, 0);
+  int nm = wave_subs(it.rows);
+  for (int gidx = 0; gidx < sc.total; ++gidx) {
+    wait_lgkm0();  // this wave's reads of the previous stage are done
+    barrier();
+    const uint8_t* as = smem + L::A + (gidx % kAStages) * A_STAGE;
+    const uint8_t* bs = smem + L::B + (gidx % BL::NBS) * BL::STAGE;
+    switch (nm) {
+      case 4: if constexpr (kMaxSub >= 4) compute_stage<WF, 4>(acc, as, bs, wm, brow0, brow1); break;
+      case 3: if constexpr (kMaxSub >= 3) compute_stage<WF, 3>(acc, as, bs, wm, brow0, brow1); break;
+      case 2: compute_stage<WF, 2>(acc, as, bs, wm, brow0, brow1); break;
+      case 1: compute_stage<WF, 1>(acc, as, bs, wm, brow0, brow1); break;
+      default: break;
+    }
+    if (++cs < sc.nk) continue;
 
-  auto epilogue = [&]() {
+    // ---- epilogue of item ci ----
+    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (ci % 3) * TABLE);
+    const float* twt = (const float*)(smem + L::TBL + (ci % 3) * TABLE + TBM * 4);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < kMaxSub; ++m) {
       if (m >= nm) continue;
-      const int sbk = wm + 4 * m;
+      const int sbk = wm + kGroupsM * m;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 32 * sbk + 8 * (i >> 2) + 4 * g + (i & 3);
@@ -333,70 +311,232 @@ __global__ __launch_bounds__(kThreads, 1) void k_fc_tiled(FcArgs p) {
 #pragma unroll
           for (int off = 1; off < 32; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
           const int sexp = block_exponent<3>(mx);
-          if (row < cit.rows) {
-            const int64_t prow = cit.p0 + row;
-            const int col0 = cit.nb * (TBN / 2) + 32 * wn;
+          if (row < it.rows) {
+            const int64_t prow = it.p0 + row;
+            const int col0 = it.nb * (TBN / 2) + 32 * wn;
             ((uint8_t*)p.out)[prow * p.N + col0 + l32] = (uint8_t)encode<3>(h * exp2_neg(sexp));
             if (l32 == 0) p.out_scale[prow * (p.N / 32) + col0 / 32] = (uint8_t)(sexp + 127);
           }
-        } else {
-          if (row < cit.rows) {
-            // routed: row of the assignment (weight applied here, in fp32);
-            // dense: row of the token
-            const int prow = cit.p0 + row;
-            int64_t orow;
-            float w;
-            if (p.dense_rows > 0) {
-              orow = prow;
-              w = p.dense_weight;
-            } else {
-              const int a = p.sorted_assign[prow];
-              orow = a;
-              w = p.topk_w[a];
-            }
-            float* o = p.obuf + orow * p.N + cit.nb * TBN + 64 * wn + l32;
-            o[0] = w * acc[m][0][i];
-            o[32] = w * acc[m][1][i];
+        } else if (row < it.rows) {
+          // routed: row of the assignment, weight applied here in fp32;
+          // dense: row of the token
+          int64_t orow;
+          float w;
+          if (p.dense_rows > 0) {
+            orow = it.p0 + row;
+            w = p.dense_weight;
+          } else {
+            orow = tsrc[row];
+            w = twt[row];
           }
+          float* o = p.obuf + orow * p.N + it.nb * TBN + 64 * wn + l32;
+          o[0] = w * acc[m][0][i];
+          o[32] = w * acc[m][1][i];
         }
       }
     }
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < kMaxSub; ++m)
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.f;
-  };
-
-  // One step: stage gidx is complete once this wave's copies for it have
-  // landed (at most D younger copies -- the next stage's -- may remain) and
-  // every wave has passed the barrier; then the stage after next is issued
-  // into the buffer read in the previous step, and stage gidx is multiplied.
-  int cur = 0;
-  for (int gidx = 0; gidx < total; ++gidx) {
-    if (gidx + 1 < total) wait_vm_lgkm0<D>();
-    else wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (gidx + 2 < total) issue_next(cur == 0 ? 2 : cur - 1);
-    const uint8_t* base = smem + cur * L::STAGE;
-    if (nm == 2) compute_stage<WF, 2>(acc, base, wm, brow0, brow1);
-    else if (nm == 1) compute_stage<WF, 1>(acc, base, wm, brow0, brow1);
-    cur = cur == 2 ? 0 : cur + 1;
-    if (++cs == nk) {
-      epilogue();
-      // the epilogue's stores are younger than the copies in flight; drain
-      // them so that the copy counts above stay exact
-      wait_vm_lgkm0<0>();
-      cs = 0;
-      if (++ci < my_items) {
-        cit = item_geom(p, xcd, q + ci * Q, NB);
-        const int nsub = (cit.rows + 31) >> 5;
-        nm = (wm < nsub) + (wm + 4 < nsub);
-      }
+    cs = 0;
+    if (++ci < sc.my_items) {
+      it = item_geom(p, sc, ci);
+      nm = wave_subs(it.rows);
     }
   }
+}
+
+// ----------------------------------------------------- activation copies ---
+
+// Copies the row table of an item (routed mode): the assignment id of each
+// tile row (FC1: turned into the token of the activation row when read; FC2:
+// the output row) and its routing weight.  Rows past the tile repeat its first
+// row.  Both activation waves copy the ids (the same bytes to the same place),
+// so each reads only what its own copies wrote; the first also copies the
+// weights, which only the multiply waves read, barriers later.
+__device__ __forceinline__ void copy_table(const FcArgs& p, const ItemGeom& it, uint32_t tbl) {
+  const int lane = threadIdx.x & 63, aw = (threadIdx.x >> 6) - kWaveA;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 64 * t + lane;
+    const int prow = it.p0 + (r < it.rows ? r : 0);
+    lds_copy4(p.sorted_assign + prow, tbl + 256 * t);
+    if (aw == 0) lds_copy4(p.sorted_w + prow, tbl + TBM * 4 + 256 * t);
+  }
+}
+
+template <bool FC1, int WF>
+__device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
+  using L = Lds<WF>;
+  const int lane = threadIdx.x & 63, aw = (threadIdx.x >> 6) - kWaveA;
+  const int K = p.K;
+  const bool routed = p.dense_rows == 0;
+  const uint32_t lds0 = lds_addr(smem);
+  const int c = (lane & 7) ^ (lane >> 3);  // chunk that lands in this lane's LDS slot
+
+  const uint8_t* asrc[16];
+  const uint8_t* ssrc[2];
+  int load_nb = 0;
+  // source rows of item li; its row table must have landed
+  auto setup = [&](int li) {
+    const ItemGeom it = item_geom(p, sc, li);
+    load_nb = it.nb;
+    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (li % 3) * TABLE);
+    auto src_row = [&](int r) -> int64_t {
+      r = r < it.rows ? r : it.rows - 1;  // rows past the tile repeat its last row
+      if (!routed) return it.p0 + r;
+      return FC1 ? tsrc[r] / p.k : (int64_t)it.p0 + r;
+    };
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = 16 * aw + i;
+      asrc[i] = (const uint8_t*)p.a + src_row(8 * t + (lane >> 3)) * K + 16 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ssrc[i] = p.a_scale + src_row(64 * (2 * aw + i) + lane) * (K / 32);
+  };
+  auto issue = [&](int s, int buf) {
+    const uint32_t base = lds0 + L::A + buf * A_STAGE;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lds_copy16(asrc[i] + s * TBK, base + 1024 * (16 * aw + i));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_copy4(ssrc[i] + 4 * s, base + A_CODES + 256 * (2 * aw + i));
+  };
+
+  // load cursor: item li, stage ls; stages issued so far
+  int li = 0, ls = 0, issued = 0;
+  if (routed) {
+    copy_table(p, item_geom(p, sc, 0), lds0 + L::TBL);
+    wait_vm_lgkm0<0>();
+  }
+  // issue the next stage; at the start of an item, first copy the next item's
+  // row table (these copies are older than the stage's, so the per-step wait
+  // below also covers them)
+  auto issue_next = [&]() {
+    if (ls == 0) {
+      if (routed && li + 1 < sc.my_items)
+        copy_table(p, item_geom(p, sc, li + 1), lds0 + L::TBL + ((li + 1) % 3) * TABLE);
+      setup(li);
+    }
+    issue(k_stage(sc, load_nb, ls), issued % kAStages);
+    ++issued;
+    if (++ls == sc.nk) {
+      ls = 0;
+      ++li;
+      // the next setup reads item li's table, copied before the stage just
+      // issued: waiting until at most one stage of copies is in flight
+      // guarantees it has landed
+      if (li < sc.my_items) wait_vm_lgkm0<kACopies>();
+    }
+  };
+  issue_next();
+  if (sc.total > 1) issue_next();
+  for (int gidx = 0; gidx < sc.total; ++gidx) {
+    // stage gidx has landed once at most the next stage's copies are in flight
+    if (gidx + 1 < sc.total) wait_vm_lgkm0<kACopies>();
+    else wait_vm_lgkm0<0>();
+    barrier();
+    if (gidx + 2 < sc.total) issue_next();
+  }
+}
+
+// --------------------------------------------------------- weight copies ---
+
+template <int WF, int N>
+__device__ __forceinline__ void wait_b_blocks(int n) {
+  // at most n stages (n <= N) of this wave's copies may stay in flight
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vm_lgkm0<N * b_copies<WF>()>();
+      return;
+    }
+    wait_b_blocks<WF, N - 1>(n);
+  } else {
+    wait_vm_lgkm0<0>();
+  }
+}
+
+template <bool FC1, int WF>
+__device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
+  using L = Lds<WF>;
+  using BL = BLay<WF>;
+  const int lane = threadIdx.x & 63, bw = (threadIdx.x >> 6) - kWaveB;
+  const int K = p.K;
+  const uint32_t lds0 = lds_addr(smem);
+  const int64_t wrow = (int64_t)K * Fmt<WF>::BITS / 8;
+
+  const uint8_t* bsrc[BL::PER_WAVE];
+  const uint8_t* ssrc;
+  int load_nb = 0;
+  auto setup = [&](int li) {
+    const ItemGeom it = item_geom(p, sc, li);
+    load_nb = it.nb;
+    const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride;
+    const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride;
+#pragma unroll
+    for (int i = 0; i < BL::PER_WAVE; ++i) {
+      const int t = BL::PER_WAVE * bw + i;  // 1-KB copy index within the stage
+      int jr, ch;
+      if (WF == 1) {
+        jr = 16 * t + (lane >> 2);
+        ch = (lane & 3) ^ ((jr >> 1) & 3);
+      } else {
+        const int cc = 64 * t + lane;
+        jr = cc / 6;
+        ch = cc % 6;
+      }
+      bsrc[i] = wb + w_row<FC1>(p, it.nb, jr) * wrow + 16 * ch;
+    }
+    ssrc = sb + w_row<FC1>(p, it.nb, 64 * bw + lane) * (K / 32);
+  };
+  int li = 0, ls = 0, issued = 0;
+  auto issue_next = [&]() {
+    if (ls == 0) setup(li);
+    const uint32_t base = lds0 + L::B + (issued % BL::NBS) * BL::STAGE;
+    const int ks = k_stage(sc, load_nb, ls);
+    const int bo = ks * (TBK * Fmt<WF>::BITS / 8);
+#pragma unroll
+    for (int i = 0; i < BL::PER_WAVE; ++i) lds_copy16(bsrc[i] + bo, base + 1024 * (BL::PER_WAVE * bw + i));
+    lds_copy4(ssrc + 4 * ks, base + BL::CODES + 256 * bw);
+    ++issued;
+    if (++ls == sc.nk) {
+      ls = 0;
+      ++li;
+    }
+  };
+  for (int s = 0; s < BL::NBS - 1 && s < sc.total; ++s) issue_next();
+  for (int gidx = 0; gidx < sc.total; ++gidx) {
+    // stage gidx has landed once at most the stages issued after it remain
+    wait_b_blocks<WF, BL::NBS - 2>(issued - 1 - gidx);
+    barrier();
+    if (issued < sc.total) issue_next();
+  }
+}
+
+}  // namespace
+
+template <bool FC1, int WF>
+__global__ __launch_bounds__(kThreads, 1) void k_fc_tiled(FcArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<WF>::TOTAL];
+  Sched sc;
+  sc.nk = p.K / TBK;
+  sc.NB = p.nchunks;
+  const int ntiles = p.dense_rows > 0 ? (p.dense_rows + TBM - 1) / TBM : *p.num_tiles;
+  sc.xcd = blockIdx.x & 7;
+  sc.q = blockIdx.x >> 3;
+  sc.Q = gridDim.x >> 3;
+  const int xt = ntiles > sc.xcd ? (ntiles - sc.xcd + 7) / 8 : 0;
+  const int nitems = xt * sc.NB;
+  sc.my_items = nitems > sc.q ? (nitems - sc.q + sc.Q - 1) / sc.Q : 0;
+  sc.total = sc.my_items * sc.nk;  // (item, stage) steps of this workgroup
+  if (sc.total == 0) return;
+  const int wv = threadIdx.x >> 6;
+  if (wv < kComputeWaves) multiply_role<FC1, WF>(p, sc, smem);
+  else if (wv < kWaveB) activation_role<FC1, WF>(p, sc, smem);
+  else weight_role<FC1, WF>(p, sc, smem);
 }
 
 template <bool FC1, int WF>

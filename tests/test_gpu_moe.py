@@ -26,6 +26,11 @@ CASES = {
     "w4a8_multi_tile": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=700, H=256, I=256, E=4, k=2),
     "w6a8_multi_tile_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=300, H=384, I=256, E=2, k=2,
                                          I_shared=256),
+    # enough (M-tile, N-block) items that every persistent workgroup of the
+    # tiled GEMMs streams several of them back to back
+    "w4a8_stream_items": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=512, H=2048, I=1024, E=32, k=4),
+    "w6a8_stream_items": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=512, H=2048, I=1024, E=32, k=4,
+                                    I_shared=1024),
 }
 
 _cache = {}
