@@ -56,4 +56,9 @@ constexpr int kTiledColsFc2 = 128;
 constexpr int kTiledMinK = 256;
 hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int grid, hipStream_t st);
 
+// Small-M variant for bf16 activations and E2M1 weights: M-tiles of up to
+// kStreamRows rows (the same tile list as the stream kernels), N-blocks of 64
+// h columns (FC1) or 128 output columns (FC2); `grid` persistent workgroups.
+hipError_t launch_fc_small(const FcArgs& p, bool fc1, int grid, hipStream_t st);
+
 }  // namespace moe_mx

@@ -65,11 +65,11 @@ __device__ __forceinline__ void load_a(AFrag& f, const uint8_t* row, const uint8
 template <int WF>
 __device__ __forceinline__ void load_b(BFrag& f, const uint8_t* row, const uint8_t* srow, int c, int g) {
   if (WF == 1) {
-    uint4 v = *(const uint4*)(row + 64 * c + 16 * g);
+    const uint4 v = *(const uint4*)(row + 64 * c + 16 * g);
     f.d[0] = v.x; f.d[1] = v.y; f.d[2] = v.z; f.d[3] = v.w; f.d[4] = 0; f.d[5] = 0;
   } else {
     const uint2* p = (const uint2*)(row + 24 * (4 * c + g));
-    uint2 a = p[0], b = p[1], d = p[2];
+    const uint2 a = p[0], b = p[1], d = p[2];
     f.d[0] = a.x; f.d[1] = a.y; f.d[2] = b.x; f.d[3] = b.y; f.d[4] = d.x; f.d[5] = d.y;
   }
   f.scale = *(const uint32_t*)(srow + 4 * c);

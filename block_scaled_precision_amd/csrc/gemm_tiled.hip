@@ -45,6 +45,7 @@
 // (row 8*(i/4) + 4*(l/32) + i%4, column l%32).
 #include <hip/hip_runtime.h>
 
+#include "copy_ring.h"
 #include "gemm.h"
 #include "mx_device.h"
 
@@ -94,34 +95,6 @@ template <int WF> struct Lds {
 constexpr int kACopies = 16 + 2;                                       // codes + scale words
 template <int WF> constexpr int b_copies() { return BLay<WF>::PER_WAVE + 1; }
 
-// s_waitcnt with vmcnt(n) and lgkmcnt(0) (gfx9 encoding; expcnt left at its maximum).
-template <int N> __device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
-
-// Asynchronous copies global -> LDS (global_load_lds): lane i of the wave writes
-// its `size` bytes at lds + size*i; `lds` is a wave-uniform LDS byte address.
-// M0 carries the LDS address; one wait state separates its write from the copy.
-__device__ __forceinline__ void lds_copy16(const uint8_t* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
-}
-__device__ __forceinline__ void lds_copy4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
-}
-
-__device__ __forceinline__ void barrier() {
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
-}
-
 // A tile: row r holds 8 chunks of 16 B; chunk c sits at slot c ^ (r & 7) so
 // that 8 consecutive rows read at the same k land in 8 different bank groups.
 __device__ __forceinline__ int a_off(int r, int c) { return r * TBK + 16 * (c ^ (r & 7)); }
@@ -135,22 +108,6 @@ struct ItemGeom {
 struct Sched {
   int xcd, q, Q, NB, nk, my_items, total;
 };
-
-// Tile-list entry through the scalar cache: a scalar load counts on lgkmcnt,
-// not on the vector memory counter that tracks the copies in flight, so
-// reading the next item's geometry never waits for them.  The load and its
-// wait sit in one asm block.
-__device__ __forceinline__ Tile load_tile(const Tile* tiles, int ti) {
-  const Tile* ptr = tiles + __builtin_amdgcn_readfirstlane(ti);
-  int4 v;
-  asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-  Tile t;
-  t.expert = v.x;
-  t.p0 = v.y;
-  t.rows = v.z;
-  t.pad = v.w;
-  return t;
-}
 
 __device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, const Sched& sc, int li) {
   const int j = sc.q + li * sc.Q;

@@ -347,11 +347,15 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.ws_estride = 2 * (int64_t)I * (H / 32);
   a1.K = H;
   a1.N = I;
-  a1.nchunks = I / (f.tiled ? kTiledColsFc1 : kStreamColsFc1);
+  // bf16 activations (E2M1 weights): the small-M kernel; MXFP8 activations:
+  // the tiled kernel when rows per expert allow, else the stream kernel
+  const bool small = !mx;
+  a1.nchunks = I / ((f.tiled || small) ? kTiledColsFc1 : kStreamColsFc1);
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
   const int cus = device_cus();
   auto launch_fc = [&](const FcArgs& a, bool fc1, bool tiled) {
+    if (small) return launch_fc_small(a, fc1, cus, stream);
     return tiled ? launch_fc_tiled(a, fc1, wf, cus, stream) : launch_fc_stream(a, fc1, mx, wf, stream);
   };
   if (!ok(launch_fc(a1, true, f.tiled))) return MOE_ERR_HIP;
@@ -366,7 +370,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a2.ws_estride = (int64_t)H * (I / 32);
   a2.K = I;
   a2.N = H;
-  a2.nchunks = H / (f.tiled ? kTiledColsFc2 : kStreamColsFc2);
+  a2.nchunks = H / ((f.tiled || small) ? kTiledColsFc2 : kStreamColsFc2);
   a2.out = nullptr;
   a2.obuf = obuf;
   if (!ok(launch_fc(a2, false, f.tiled))) return MOE_ERR_HIP;
@@ -381,7 +385,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s1.w_estride = 0;
     s1.ws_estride = 0;
     s1.N = Is;
-    s1.nchunks = Is / (f.shared_tiled ? kTiledColsFc1 : kStreamColsFc1);
+    s1.nchunks = Is / ((f.shared_tiled || small) ? kTiledColsFc1 : kStreamColsFc1);
     s1.out = ws + f.hs;
     s1.out_scale = (uint8_t*)(ws + f.hssc);
     if (!ok(launch_fc(s1, true, f.shared_tiled))) return MOE_ERR_HIP;
@@ -395,7 +399,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s2.w_estride = 0;
     s2.ws_estride = 0;
     s2.K = Is;
-    s2.nchunks = H / (f.shared_tiled ? kTiledColsFc2 : kStreamColsFc2);
+    s2.nchunks = H / ((f.shared_tiled || small) ? kTiledColsFc2 : kStreamColsFc2);
     s2.obuf = sbuf;
     (void)bytes_is;
     if (!ok(launch_fc(s2, false, f.shared_tiled))) return MOE_ERR_HIP;
