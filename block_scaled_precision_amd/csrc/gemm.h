@@ -59,6 +59,8 @@ hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int grid, hipStr
 // Small-M variant for bf16 activations and E2M1 weights: M-tiles of up to
 // kStreamRows rows (the same tile list as the stream kernels), N-blocks of 64
 // h columns (FC1) or 128 output columns (FC2); `grid` persistent workgroups.
+// Requires K % kSmallK == 0.
+constexpr int kSmallK = 256;
 hipError_t launch_fc_small(const FcArgs& p, bool fc1, int grid, hipStream_t st);
 
 }  // namespace moe_mx

@@ -7,14 +7,16 @@
 //
 // Work item = (16-row M-tile of one expert, N-block of 128 weight rows: FC1
 // 64 gate + 64 up rows, i.e. 64 columns of h; FC2 128 output columns).  The
-// grid is persistent (one workgroup per CU).  Per 128-K stage the weight
-// tile (128 rows x 64 B of E2M1 codes + one E8M0 scale word per row) and the
-// activation tile (16 rows x 256 B of bf16) are copied global -> LDS into a
-// ring of 12 stage buffers, so up to 11 stages (about 100 KB per CU) are in
-// flight: enough to cover HBM latency at full bandwidth.
+// grid is persistent (one workgroup per CU).  Per 256-K stage the weight
+// tile (128 rows x 128 B of E2M1 codes + 8 E8M0 scale bytes per row) and the
+// activation tile (16 rows x 512 B of bf16) are copied global -> LDS into a
+// ring of 6 stage buffers, so up to 5 stages (about 100 KB per CU) are in
+// flight: enough to cover HBM latency at full bandwidth.  Reading 128
+// contiguous bytes of every weight row per stage streams HBM markedly faster
+// than 64 (measured: the decode FC1 went from 4.7 to 5.5 TB/s).
 //
-// Waves (7): 0-3 multiply, 4-5 copy weights (5 copies per stage each), 6 copies
-// activations (4 copies per stage).  Each copy wave owns one in-order stream
+// Waves (7): 0-3 multiply, 4-5 copy weights (10 copies per stage each), 6
+// copies activations (8 copies per stage).  Each copy wave owns one in-order stream
 // and waits for its own stage before the per-stage barrier; the multiply
 // waves issue no loads (item geometry and row metadata come through the
 // scalar cache).
@@ -22,9 +24,9 @@
 // MFMA: v_mfma_f32_16x16x32_bf16 (lane l supplies row l%16 and 8 consecutive
 // k-slots 8*(l/16) .. +8; accumulator element i of lane l is (row 4*(l/16)+i,
 // column l%16)).  The contraction order is free, so lane group g = l/16 takes
-// the actual k range [32g, 32g + 32) of the stage, 8 values per MFMA step: its
-// weight bytes are one 16-B chunk (one MX block, one scale byte) and its
-// activation values one 64-B run.  Weights are dequantized in registers with
+// the actual k range [64g, 64g + 64) of the stage, 8 values per MFMA step: its
+// weight bytes are two 16-B chunks (two MX blocks, two scale bytes) and its
+// activation values one 128-B run.  Weights are dequantized in registers with
 // v_cvt_scalef32_pk_bf16_fp4 (exact for E8M0 scales).
 #include <hip/hip_runtime.h>
 
@@ -36,27 +38,38 @@ namespace moe_mx {
 
 namespace {
 
+#ifndef MOE_SMALL_BK
+#define MOE_SMALL_BK 256
+#endif
 constexpr int SBM = kStreamRows;  // 16 rows per M-tile
 constexpr int SBN = 128;          // weight rows per item
-constexpr int SBK = 128;          // K per stage
-constexpr int NSTAGE = 12;        // ring depth
+constexpr int SBK = MOE_SMALL_BK; // K per stage (128 or 256)
+static_assert(SBK == kSmallK, "the host checks K divisibility against kSmallK");
+constexpr int NSTAGE = SBK == 128 ? 12 : 6;  // ring depth (about 150 KB either way)
+constexpr int KPL = SBK / 4;      // k values per lane group and stage (one or two MX blocks)
+constexpr int BROW = SBK / 2;     // weight bytes per row and stage
 constexpr int kMulW = 4;
 constexpr int kWaveB = 4;         // weight-copy waves 4, 5
 constexpr int kWaveA = 6;         // activation-copy wave
 constexpr int kThreadsS = 64 * 7;
 
-// stage layout: [weights 128 x 64 B][scale words 128 x 4 B][activations 16 x 256 B]
-constexpr int S_B = SBN * SBK / 2;
-constexpr int S_BS = SBN * 4;
+// stage layout: [weights 128 rows x BROW][scale bytes 128 rows x SBK/32]
+//               [activations 16 rows x 2*SBK]
+constexpr int S_B = SBN * BROW;
+constexpr int S_BS = SBN * SBK / 32;
 constexpr int S_A = SBM * SBK * 2;
 constexpr int S_STAGE = S_B + S_BS + S_A;
-constexpr int kBCopies = S_B / 1024 / 2 + 1;  // per weight-copy wave: 4 x 1 KB + 1 scale copy
-constexpr int kACopiesS = S_A / 1024;         // 4 x 1 KB
+constexpr int kBData = S_B / 1024 / 2;        // 1-KB weight copies per weight-copy wave
+constexpr int kBScale = S_BS / 256 / 2;       // 256-B scale copies per weight-copy wave
+constexpr int kBCopies = kBData + kBScale;
+constexpr int kACopiesS = S_A / 1024;
 
-// weight tile: 16-B chunk c of row r at slot c ^ ((r >> 1) & 3)
-__device__ __forceinline__ int wb_off(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
+// weight tile: 16-B chunk c of row r at slot c ^ swz(r), so that 8 rows read
+// at the same chunk fall in 8 different 16-B bank groups
+__device__ __forceinline__ int wb_swz(int r) { return BROW == 64 ? ((r >> 1) & 3) : (r & 7); }
+__device__ __forceinline__ int wb_off(int r, int c) { return r * BROW + 16 * (c ^ wb_swz(r)); }
 // activation tile: 16-B chunk c (8 bf16) of row r at slot c ^ (r & 7)
-__device__ __forceinline__ int wa_off(int r, int c) { return r * 256 + 16 * (c ^ (r & 7)); }
+__device__ __forceinline__ int wa_off(int r, int c) { return r * (2 * SBK) + 16 * (c ^ (r & 7)); }
 
 struct SGeom {
   int expert, p0, rows, nb;
@@ -119,28 +132,34 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
     wait_lgkm0();
     barrier();
     const uint8_t* st = smem + (gidx % NSTAGE) * S_STAGE;
-    const uint32_t* sw = (const uint32_t*)(st + S_B);
+    const uint8_t* sb = st + S_B;
     const uint8_t* as = st + S_B + S_BS;
-    // activation run of this lane: row r16, k [32g, 32g + 32) = chunks 4g .. 4g+3
-    uint4 a[4];
+    // activation run of this lane: row r16, k [KPL*g, KPL*(g+1)) = chunks
+    // (KPL/8)*g .. +KPL/8
+    constexpr int NA = KPL / 8;  // 16-B activation chunks (MFMA steps) per lane
+    uint4 a[NA];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[ks] = *(const uint4*)(as + wa_off(r16, 4 * g + ks));
+    for (int ks = 0; ks < NA; ++ks) a[ks] = *(const uint4*)(as + wa_off(r16, NA * g + ks));
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int jr = (n == 0 ? t0 : t1) + r16;
-      const uint4 b = *(const uint4*)(st + wb_off(jr, g));
-      const float sc = e8m0_to_f32((sw[jr] >> (8 * g)) & 0xffu);
-      const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const v2bf q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[ks], sc, 0);
-        const v2bf q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[ks], sc, 1);
-        const v2bf q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[ks], sc, 2);
-        const v2bf q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[ks], sc, 3);
-        const v8bf bv = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
-        v8bf av;
-        __builtin_memcpy(&av, &a[ks], 16);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[n], 0, 0, 0);
+      for (int blk = 0; blk < KPL / 32; ++blk) {
+        // one MX block: 16 B of codes, one scale byte
+        const uint4 b = *(const uint4*)(st + wb_off(jr, (KPL / 32) * g + blk));
+        const float sc = e8m0_to_f32(sb[jr * (SBK / 32) + (KPL / 32) * g + blk]);
+        const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+          const v2bf q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[kq], sc, 0);
+          const v2bf q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[kq], sc, 1);
+          const v2bf q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[kq], sc, 2);
+          const v2bf q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(bw[kq], sc, 3);
+          const v8bf bv = {q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+          v8bf av;
+          __builtin_memcpy(&av, &a[4 * blk + kq], 16);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[n], 0, 0, 0);
+        }
       }
     }
     if (++cs < sc.nk) continue;
@@ -204,28 +223,37 @@ __device__ __forceinline__ void small_weights(const FcArgs& p, const SSched& sc,
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
   const int64_t wrow = (int64_t)K / 2;
-  const uint8_t* src[4];
-  const uint8_t* ssrc;
+  constexpr int CPR = BROW / 16;  // 16-B chunks per weight row and stage
+  const uint8_t* src[kBData];
+  const uint8_t* ssrc[kBScale];
   auto setup = [&](int li) {
     const SGeom it = s_geom(p, sc, li);
     const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride;
     const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 4 * bw + i;
-      const int jr = 16 * t + (lane >> 2);
-      const int ch = (lane & 3) ^ ((jr >> 1) & 3);
+    for (int i = 0; i < kBData; ++i) {
+      const int t = kBData * bw + i;  // 1-KB copy index within the stage
+      const int jr = (64 / CPR) * t + lane / CPR;
+      const int ch = (lane % CPR) ^ wb_swz(jr);
       src[i] = wb + s_wrow<FC1>(p, it.nb, jr) * wrow + 16 * ch;
     }
-    ssrc = sb + s_wrow<FC1>(p, it.nb, 64 * bw + lane) * (K / 32);
+    // scale bytes: SBK/32 per row and stage; one 4-B lane covers 4 / (SBK/32) rows
+#pragma unroll
+    for (int i = 0; i < kBScale; ++i) {
+      const int t = kBScale * bw + i;       // 256-B scale copy index
+      const int byte = 256 * t + 4 * lane;  // offset in the stage's scale area
+      const int jr = byte / (SBK / 32), within = byte % (SBK / 32);
+      ssrc[i] = sb + s_wrow<FC1>(p, it.nb, jr) * (K / 32) + within;
+    }
   };
   int li = 0, ls = 0, issued = 0;
   auto issue_next = [&]() {
     if (ls == 0) setup(li);
     const uint32_t base = lds0 + (issued % NSTAGE) * S_STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_copy16(src[i] + ls * (SBK / 2), base + 1024 * (4 * bw + i));
-    lds_copy4(ssrc + 4 * ls, base + S_B + 256 * bw);
+    for (int i = 0; i < kBData; ++i) lds_copy16(src[i] + ls * BROW, base + 1024 * (kBData * bw + i));
+#pragma unroll
+    for (int i = 0; i < kBScale; ++i) lds_copy4(ssrc[i] + ls * (SBK / 32), base + S_B + 256 * (kBScale * bw + i));
     ++issued;
     if (++ls == sc.nk) {
       ls = 0;
@@ -248,7 +276,9 @@ __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched&
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
   const bool gather = FC1 && p.dense_rows == 0;
-  const uint8_t* src[4];
+  constexpr int RPC = 1024 / (2 * SBK);  // activation rows per 1-KB copy
+  constexpr int CPA = 2 * SBK / 16;      // 16-B chunks per activation row and stage
+  const uint8_t* src[kACopiesS];
   auto setup = [&](int li) {
     const SGeom it = s_geom(p, sc, li);
     int tok[16];
@@ -258,10 +288,10 @@ __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched&
       for (int q = 0; q < 16; ++q) tok[q] = ids.v[q] / p.k;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // copy i lands rows 4i .. 4i+3; rows past the tile repeat its first row
-      int r = 4 * i + (lane >> 4);
-      r = r < it.rows ? r : 0;
+    for (int i = 0; i < kACopiesS; ++i) {
+      // copy i lands rows RPC*i ..; rows past the tile repeat its first row
+      const int lr = RPC * i + lane / CPA;  // LDS row
+      const int r = lr < it.rows ? lr : 0;
       int64_t row = it.p0 + r;
       if (gather) {
         int tr = tok[0];
@@ -270,7 +300,7 @@ __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched&
           if (r == q) tr = tok[q];
         row = tr;
       }
-      const int c = (lane & 15) ^ ((4 * i + (lane >> 4)) & 7);  // chunk for this lane's LDS slot
+      const int c = (lane % CPA) ^ (lr & 7);  // chunk for this lane's LDS slot
       src[i] = (const uint8_t*)p.a + row * (2 * (int64_t)K) + 16 * c;
     }
   };
@@ -279,7 +309,7 @@ __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched&
     if (ls == 0) setup(li);
     const uint32_t base = lds0 + (issued % NSTAGE) * S_STAGE + S_B + S_BS;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_copy16(src[i] + ls * (2 * SBK), base + 1024 * i);
+    for (int i = 0; i < kACopiesS; ++i) lds_copy16(src[i] + ls * (2 * SBK), base + 1024 * i);
     ++issued;
     if (++ls == sc.nk) {
       ls = 0;

@@ -349,7 +349,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.N = I;
   // bf16 activations (E2M1 weights): the small-M kernel; MXFP8 activations:
   // the tiled kernel when rows per expert allow, else the stream kernel
-  const bool small = !mx;
+  const bool small = !mx && H % kSmallK == 0 && I % kSmallK == 0 && Is % kSmallK == 0;
   a1.nchunks = I / ((f.tiled || small) ? kTiledColsFc1 : kStreamColsFc1);
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
