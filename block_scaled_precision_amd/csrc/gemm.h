@@ -50,7 +50,7 @@ hipError_t launch_fc_stream(const FcArgs& p, bool fc1, bool mx_act, int wfmt, hi
 // of 64 h columns (FC1: nchunks = I / 64) or 128 output columns (FC2:
 // nchunks = H / 128); `grid` persistent workgroups (rounded down to a multiple
 // of 8, at least 8).  Requires K >= kTiledMinK.
-constexpr int kTiledRows = 256;
+constexpr int kTiledRows = 192;
 constexpr int kTiledColsFc1 = 64;
 constexpr int kTiledColsFc2 = 128;
 constexpr int kTiledMinK = 256;

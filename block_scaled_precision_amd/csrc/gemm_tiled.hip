@@ -5,13 +5,14 @@
 // values, block-scaled MMA with FP32 accumulation; TokenSpeed SiTU page,
 // "Activation precision": MXFP8 activation x MXFP4 weight).
 //
-// Work item = (M-tile, N-block).  An M-tile holds up to 256 permuted rows of one
-// expert, so an expert with <= 256 assignments streams its weights from HBM
+// Work item = (M-tile, N-block).  An M-tile holds up to 192 permuted rows of one
+// expert, so an expert with <= 192 assignments streams its weights from HBM
 // exactly once; the N-block is 128 weight rows (FC1: 64 gate rows and the 64
 // matching up rows, i.e. 64 columns of h; FC2: 128 output columns).  The grid is
-// persistent: one workgroup per CU walks the items of its XCD (the M-tiles x,
-// x+8, ... of XCD x), so the N-blocks of one M-tile run together on one XCD and
-// its activation rows stay in that XCD's L2.  Items are consumed as one
+// persistent: one workgroup per CU walks the items of its XCD (whole M-tiles
+// x, x+8, ..., then an equal share of the N-blocks of the last ntiles % 8
+// tiles), so the N-blocks of one M-tile run together on one XCD and its
+// activation rows stay in that XCD's L2.  Items are consumed as one
 // continuous stream of (item, 128-K stage) steps with one workgroup barrier per
 // step.
 //
@@ -21,8 +22,8 @@
 //    spreads over all SIMDs) and two 32-column MFMA tiles, reads its operands
 //    from LDS and writes the item's results;
 //  * waves 8-9 copy the activation stage (gathered rows of E4M3 codes, 128 B per
-//    row and stage, plus the per-row scale words) into a ring of 3 LDS
-//    buffers, two stages ahead of the multiply;
+//    row and stage, plus the per-row scale words) into a ring of 4 LDS
+//    buffers, three stages ahead of the multiply;
 //  * waves 10-11 copy the weight stage (64 B per row and stage for E2M1, 96 B
 //    for E3M2, plus scale words) into a deeper ring (6 buffers for E2M1, 4 for
 //    E3M2) so that weights, which come from HBM, are requested 5 (3) stages
@@ -55,7 +56,7 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int TBM = kTiledRows;  // rows per M-tile (8 sub-blocks of 32)
+constexpr int TBM = kTiledRows;  // rows per M-tile (6 sub-blocks of 32)
 constexpr int TBN = 128;         // weight rows per work item
 constexpr int TBK = 128;         // K per stage
 #ifndef MOE_TILED_MUL_WAVES
@@ -67,12 +68,16 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveA = kComputeWaves;      // first activation-copy wave
 constexpr int kWaveB = kComputeWaves + 2;  // first weight-copy wave
 constexpr int kGroupsM = kComputeWaves / 2;  // multiply waves along M
-constexpr int kMaxSub = 8 / kGroupsM;        // 32-row sub-blocks per multiply wave
+constexpr int kMaxSub = (kTiledRows / 32 + kGroupsM - 1) / kGroupsM;  // 32-row sub-blocks per multiply wave
 
-// LDS layout: [A ring: 3 x (codes 32 KB + scale words 1 KB)]
+// LDS layout: [A ring: 4 x (codes TBM x 128 B + scale words TBM x 4 B)]
 //             [B ring: NBS x (weights + scale words 512 B)]
-//             [row tables: 3 x (source row 1 KB + weight 1 KB)]
-constexpr int kAStages = 3;
+//             [row tables: 4 x (source row TBM x 4 B + weight TBM x 4 B)]
+constexpr int kAStages = 4;
+constexpr int kTables = 4;
+static_assert(TBM % 64 == 0 && TBM <= 256, "tile rows");
+constexpr int kACodeCopies = TBM / 16;  // 1-KB code copies per activation-copy wave
+constexpr int kAScaleCopies = TBM / 64; // 256-B scale copies in a stage (both waves)
 constexpr int A_CODES = TBM * TBK;
 constexpr int A_STAGE = A_CODES + TBM * 4;
 template <int WF> struct BLay {
@@ -88,11 +93,11 @@ template <int WF> struct Lds {
   static constexpr int A = 0;
   static constexpr int B = kAStages * A_STAGE;
   static constexpr int TBL = B + BLay<WF>::NBS * BLay<WF>::STAGE;
-  static constexpr int TOTAL = TBL + 3 * TABLE;
+  static constexpr int TOTAL = TBL + kTables * TABLE;
 };
 
-// copies per copy-wave and stage
-constexpr int kACopies = 16 + 2;                                       // codes + scale words
+// copies per copy-wave and stage: codes + two scale-word copies
+constexpr int kACopies = kACodeCopies + 2;
 template <int WF> constexpr int b_copies() { return BLay<WF>::PER_WAVE + 1; }
 
 // A tile: row r holds 8 chunks of 16 B; chunk c sits at slot c ^ (r & 7) so
@@ -101,19 +106,45 @@ __device__ __forceinline__ int a_off(int r, int c) { return r * TBK + 16 * (c ^ 
 // E2M1 B tile: 4 chunks per 64-B row, chunk c at slot c ^ ((r >> 1) & 3).
 __device__ __forceinline__ int b4_off(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
 
+// at most n (<= N) stages of COPIES copies each may stay in flight (copies
+// issued before them, such as row tables, are waited for as well)
+template <int COPIES, int N>
+__device__ __forceinline__ void wait_stages(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vm_lgkm0<N * COPIES>();
+      return;
+    }
+    wait_stages<COPIES, N - 1>(n);
+  } else {
+    wait_vm_lgkm0<0>();
+  }
+}
+
 struct ItemGeom {
   int expert, p0, rows, nb;
 };
 
+// Item list of one XCD: first the N-blocks of M-tiles xcd, xcd+8, ... for the
+// 8*full leading tiles (whole tiles per XCD, so an M-tile's activation rows are
+// shared in one L2), then an equal contiguous share [tail0, tail0 + ntail) of
+// the N-blocks of the ntiles % 8 remaining tiles.
 struct Sched {
-  int xcd, q, Q, NB, nk, my_items, total;
+  int xcd, full, tail0, q, Q, NB, nk, my_items, total;
 };
 
 __device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, const Sched& sc, int li) {
   const int j = sc.q + li * sc.Q;
-  const int ti = sc.xcd + 8 * (j / sc.NB);
+  int ti;
   ItemGeom g;
-  g.nb = j % sc.NB;
+  if (j < sc.full * sc.NB) {
+    ti = sc.xcd + 8 * (j / sc.NB);
+    g.nb = j % sc.NB;
+  } else {
+    const int u = sc.tail0 + j - sc.full * sc.NB;
+    ti = 8 * sc.full + u / sc.NB;
+    g.nb = u % sc.NB;
+  }
   if (p.dense_rows > 0) {
     g.expert = 0;
     g.p0 = TBM * ti;
@@ -251,8 +282,8 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
     if (++cs < sc.nk) continue;
 
     // ---- epilogue of item ci ----
-    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (ci % 3) * TABLE);
-    const float* twt = (const float*)(smem + L::TBL + (ci % 3) * TABLE + TBM * 4);
+    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (ci % kTables) * TABLE);
+    const float* twt = (const float*)(smem + L::TBL + (ci % kTables) * TABLE + TBM * 4);
 #pragma unroll
     for (int m = 0; m < kMaxSub; ++m) {
       if (m >= nm) continue;
@@ -317,7 +348,7 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
 __device__ __forceinline__ void copy_table(const FcArgs& p, const ItemGeom& it, uint32_t tbl) {
   const int lane = threadIdx.x & 63, aw = (threadIdx.x >> 6) - kWaveA;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < TBM / 64; ++t) {
     const int r = 64 * t + lane;
     const int prow = it.p0 + (r < it.rows ? r : 0);
     lds_copy4(p.sorted_assign + prow, tbl + 256 * t);
@@ -334,33 +365,36 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
   const uint32_t lds0 = lds_addr(smem);
   const int c = (lane & 7) ^ (lane >> 3);  // chunk that lands in this lane's LDS slot
 
-  const uint8_t* asrc[16];
+  const uint8_t* asrc[kACodeCopies];
   const uint8_t* ssrc[2];
   int load_nb = 0;
   // source rows of item li; its row table must have landed
   auto setup = [&](int li) {
     const ItemGeom it = item_geom(p, sc, li);
     load_nb = it.nb;
-    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (li % 3) * TABLE);
+    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (li % kTables) * TABLE);
     auto src_row = [&](int r) -> int64_t {
       r = r < it.rows ? r : it.rows - 1;  // rows past the tile repeat its last row
       if (!routed) return it.p0 + r;
       return FC1 ? tsrc[r] / p.k : (int64_t)it.p0 + r;
     };
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = 16 * aw + i;
+    for (int i = 0; i < kACodeCopies; ++i) {
+      const int t = kACodeCopies * aw + i;
       asrc[i] = (const uint8_t*)p.a + src_row(8 * t + (lane >> 3)) * K + 16 * c;
     }
+    // scale copies: wave 0 takes 0, 1 and wave 1 takes 2, 3 (a missing one
+    // repeats the last: the same bytes to the same place)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ssrc[i] = p.a_scale + src_row(64 * (2 * aw + i) + lane) * (K / 32);
+    for (int i = 0; i < 2; ++i) ssrc[i] = p.a_scale + src_row(64 * min(2 * aw + i, kAScaleCopies - 1) + lane) * (K / 32);
   };
   auto issue = [&](int s, int buf) {
     const uint32_t base = lds0 + L::A + buf * A_STAGE;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) lds_copy16(asrc[i] + s * TBK, base + 1024 * (16 * aw + i));
+    for (int i = 0; i < kACodeCopies; ++i) lds_copy16(asrc[i] + s * TBK, base + 1024 * (kACodeCopies * aw + i));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_copy4(ssrc[i] + 4 * s, base + A_CODES + 256 * (2 * aw + i));
+    for (int i = 0; i < 2; ++i)
+      lds_copy4(ssrc[i] + 4 * s, base + A_CODES + 256 * min(2 * aw + i, kAScaleCopies - 1));
   };
 
   // load cursor: item li, stage ls; stages issued so far
@@ -375,7 +409,7 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
   auto issue_next = [&]() {
     if (ls == 0) {
       if (routed && li + 1 < sc.my_items)
-        copy_table(p, item_geom(p, sc, li + 1), lds0 + L::TBL + ((li + 1) % 3) * TABLE);
+        copy_table(p, item_geom(p, sc, li + 1), lds0 + L::TBL + ((li + 1) % kTables) * TABLE);
       setup(li);
     }
     issue(k_stage(sc, load_nb, ls), issued % kAStages);
@@ -389,32 +423,18 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
       if (li < sc.my_items) wait_vm_lgkm0<kACopies>();
     }
   };
-  issue_next();
-  if (sc.total > 1) issue_next();
+  for (int s = 0; s < kAStages - 1 && s < sc.total; ++s) issue_next();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
-    // stage gidx has landed once at most the next stage's copies are in flight
-    if (gidx + 1 < sc.total) wait_vm_lgkm0<kACopies>();
-    else wait_vm_lgkm0<0>();
+    // stage gidx has landed once at most the stages issued after it remain
+    wait_stages<kACopies, kAStages - 2>(issued - 1 - gidx);
     barrier();
-    if (gidx + 2 < sc.total) issue_next();
+    if (issued < sc.total) issue_next();
   }
 }
 
 // --------------------------------------------------------- weight copies ---
 
-template <int WF, int N>
-__device__ __forceinline__ void wait_b_blocks(int n) {
-  // at most n stages (n <= N) of this wave's copies may stay in flight
-  if constexpr (N > 0) {
-    if (n >= N) {
-      wait_vm_lgkm0<N * b_copies<WF>()>();
-      return;
-    }
-    wait_b_blocks<WF, N - 1>(n);
-  } else {
-    wait_vm_lgkm0<0>();
-  }
-}
+
 
 template <bool FC1, int WF>
 __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
@@ -467,7 +487,7 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
   for (int s = 0; s < BL::NBS - 1 && s < sc.total; ++s) issue_next();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     // stage gidx has landed once at most the stages issued after it remain
-    wait_b_blocks<WF, BL::NBS - 2>(issued - 1 - gidx);
+    wait_stages<b_copies<WF>(), BL::NBS - 2>(issued - 1 - gidx);
     barrier();
     if (issued < sc.total) issue_next();
   }
@@ -485,8 +505,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fc_tiled(FcArgs p) {
   sc.xcd = blockIdx.x & 7;
   sc.q = blockIdx.x >> 3;
   sc.Q = gridDim.x >> 3;
-  const int xt = ntiles > sc.xcd ? (ntiles - sc.xcd + 7) / 8 : 0;
-  const int nitems = xt * sc.NB;
+  sc.full = ntiles / 8;
+  const int tail_items = (ntiles % 8) * sc.NB;
+  sc.tail0 = tail_items * sc.xcd / 8;
+  const int nitems = sc.full * sc.NB + tail_items * (sc.xcd + 1) / 8 - sc.tail0;
   sc.my_items = nitems > sc.q ? (nitems - sc.q + sc.Q - 1) / sc.Q : 0;
   sc.total = sc.my_items * sc.nk;  // (item, stage) steps of this workgroup
   if (sc.total == 0) return;
