@@ -225,6 +225,9 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[kMaxSub][2], const uin
       av[kk][m] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
   }
+  // every fragment read of the stage is issued before the first MFMA (the
+  // compiler would otherwise reuse one register set and wait between MFMAs)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const int sh = 8 * (2 * kk + g);
