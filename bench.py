@@ -299,7 +299,7 @@ def main():
                   "active_experts": work["active_experts"], "stages_ms": stage_ms},
     }
     if not args.no_cpu_baseline:
-        ntok = args.cpu_sample_tokens or {"tiny_w4a16": 16, "decode_w4a16": 4, "prefill_w4a8": 4,
+        ntok = args.cpu_sample_tokens or {"tiny_w4a16": 16, "decode_w4a16": 8, "prefill_w4a8": 4,
                                           "skew_w4a16": 8, "w6a8_shared": 4}[w.name]
         print(f"# cpu oracle on {ntok} tokens", file=sys.stderr, flush=True)
         cb, par = cpu_baseline(torch, np, gen, w, args.seed, logits, x, y, ntok)
