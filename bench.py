@@ -44,7 +44,7 @@ BOUND = {
 FC1_KERNEL = {
     "tiny_w4a16": "k_fc_small<true>",
     "decode_w4a16": "k_fc_small<true>",
-    "prefill_w4a8": "k_fc_tiled<true, 1>",
+    "prefill_w4a8": "k_fc_wide<true>",
     "skew_w4a16": "k_fc_small<true>",
     "w6a8_shared": "k_fc_tiled<true, 2>",
 }
@@ -52,8 +52,8 @@ FC1_KERNEL = {
 # Sources of the GEMM kernels: a committed HBM-traffic summary counts only
 # while these are unchanged since it was taken.
 KERNEL_SOURCES = tuple(f"block_scaled_precision_amd/csrc/{f}" for f in (
-    "copy_ring.h", "gemm.h", "gemm_small.hip", "gemm_stream.hip", "gemm_tiled.hip", "internal.h",
-    "mx_device.h"))
+    "copy_ring.h", "gemm.h", "gemm_small.hip", "gemm_stream.hip", "gemm_tiled.hip", "gemm_wide.hip",
+    "internal.h", "mx_device.h"))
 
 
 def parse():

@@ -35,6 +35,17 @@ __device__ __forceinline__ void lds_copy4(const void* src, uint32_t lds) {
                :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src) : "memory");
 }
 
+// The same copies from a wave-uniform base (scalar registers) plus a 32-bit
+// per-lane byte offset: no 64-bit per-lane address.
+__device__ __forceinline__ void lds_copy16_s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base) : "memory");
+}
+__device__ __forceinline__ void lds_copy4_s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base) : "memory");
+}
+
 // Workgroup barrier with no memory fence (the waits above do the ordering).
 __device__ __forceinline__ void barrier() {
   __builtin_amdgcn_s_barrier();

@@ -56,6 +56,14 @@ constexpr int kTiledColsFc2 = 128;
 constexpr int kTiledMinK = 256;
 hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int grid, hipStream_t st);
 
+// Wide variant (MXFP8 activations x E2M1 weights): M-tiles of up to kTiledRows
+// rows, N-blocks of kWideCols weight rows, i.e. 128 h columns (FC1: nchunks =
+// I / 128) or 256 output columns (FC2: nchunks = H / 256); `grid` persistent
+// workgroups (rounded down to a multiple of 8, at least 8).  Requires
+// K % 128 == 0 and K >= 256.
+constexpr int kWideCols = 256;
+hipError_t launch_fc_wide(const FcArgs& p, bool fc1, int grid, hipStream_t st);
+
 // Small-M variant for bf16 activations and E2M1 weights: M-tiles of up to
 // kStreamRows rows (the same tile list as the stream kernels), N-blocks of 64
 // h columns (FC1) or 128 output columns (FC2); `grid` persistent workgroups.

@@ -114,7 +114,7 @@ constexpr int kTiledMinRowsPerExpert = 16;
 struct FusedPlan {
   int L, off;
   int64_t A;
-  bool tiled, shared_tiled;
+  bool tiled, shared_tiled, wide, shared_wide;
   int bm;
   int nblk, max_tiles;
   size_t ids, w, rank, hist, offsets, sorted, sorted_w, tiles, ntiles, xq, xs, h, hsc, hs, hssc, obuf, sbuf, total;
@@ -130,6 +130,9 @@ static FusedPlan plan(const moe_problem_t& p) {
   f.tiled = mxa && f.L > 0 && f.A >= (int64_t)kTiledMinRowsPerExpert * f.L && p.H >= kTiledMinK &&
             p.I >= kTiledMinK;
   f.shared_tiled = mxa && p.T >= kTiledMinRowsPerExpert && p.H >= kTiledMinK && p.I_shared >= kTiledMinK;
+  // E2M1 weights take the wide tiled kernel (256-row weight blocks)
+  f.wide = f.tiled && p.w_fmt == MX_E2M1 && p.H % kWideCols == 0;
+  f.shared_wide = f.shared_tiled && p.w_fmt == MX_E2M1 && p.H % kWideCols == 0;
   f.bm = f.tiled ? kTiledRows : kStreamRows;
   f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
@@ -350,15 +353,23 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   // bf16 activations (E2M1 weights): the small-M kernel; MXFP8 activations:
   // the tiled kernel when rows per expert allow, else the stream kernel
   const bool small = !mx && H % kSmallK == 0 && I % kSmallK == 0 && Is % kSmallK == 0;
-  a1.nchunks = I / ((f.tiled || small) ? kTiledColsFc1 : kStreamColsFc1);
+  // N-block width of each variant: FC1 in h columns, FC2 in output columns
+  auto cols_fc1 = [&](bool tiled, bool wide) {
+    return wide ? kWideCols / 2 : ((tiled || small) ? kTiledColsFc1 : kStreamColsFc1);
+  };
+  auto cols_fc2 = [&](bool tiled, bool wide) {
+    return wide ? kWideCols : ((tiled || small) ? kTiledColsFc2 : kStreamColsFc2);
+  };
+  a1.nchunks = I / cols_fc1(f.tiled, f.wide);
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
   const int cus = device_cus();
-  auto launch_fc = [&](const FcArgs& a, bool fc1, bool tiled) {
+  auto launch_fc = [&](const FcArgs& a, bool fc1, bool tiled, bool wide) {
     if (small) return launch_fc_small(a, fc1, cus, stream);
+    if (wide) return launch_fc_wide(a, fc1, cus, stream);
     return tiled ? launch_fc_tiled(a, fc1, wf, cus, stream) : launch_fc_stream(a, fc1, mx, wf, stream);
   };
-  if (!ok(launch_fc(a1, true, f.tiled))) return MOE_ERR_HIP;
+  if (!ok(launch_fc(a1, true, f.tiled, f.wide))) return MOE_ERR_HIP;
   // 6-7. FC2 + weighted combine into the fp32 accumulator
   if (!mark(MOE_STAGE_FC2)) return MOE_ERR_HIP;
   FcArgs a2 = a1;
@@ -370,10 +381,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a2.ws_estride = (int64_t)H * (I / 32);
   a2.K = I;
   a2.N = H;
-  a2.nchunks = H / ((f.tiled || small) ? kTiledColsFc2 : kStreamColsFc2);
+  a2.nchunks = H / cols_fc2(f.tiled, f.wide);
   a2.out = nullptr;
   a2.obuf = obuf;
-  if (!ok(launch_fc(a2, false, f.tiled))) return MOE_ERR_HIP;
+  if (!ok(launch_fc(a2, false, f.tiled, f.wide))) return MOE_ERR_HIP;
   // shared expert: a dense expert over all T tokens with its own weight
   if (!mark(MOE_STAGE_SHARED)) return MOE_ERR_HIP;
   if (Is > 0) {
@@ -385,10 +396,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s1.w_estride = 0;
     s1.ws_estride = 0;
     s1.N = Is;
-    s1.nchunks = Is / ((f.shared_tiled || small) ? kTiledColsFc1 : kStreamColsFc1);
+    s1.nchunks = Is / cols_fc1(f.shared_tiled, f.shared_wide);
     s1.out = ws + f.hs;
     s1.out_scale = (uint8_t*)(ws + f.hssc);
-    if (!ok(launch_fc(s1, true, f.shared_tiled))) return MOE_ERR_HIP;
+    if (!ok(launch_fc(s1, true, f.shared_tiled, f.shared_wide))) return MOE_ERR_HIP;
     FcArgs s2 = a2;
     s2.dense_rows = T;
     s2.dense_weight = p->shared_weight;
@@ -399,10 +410,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s2.w_estride = 0;
     s2.ws_estride = 0;
     s2.K = Is;
-    s2.nchunks = H / ((f.shared_tiled || small) ? kTiledColsFc2 : kStreamColsFc2);
+    s2.nchunks = H / cols_fc2(f.shared_tiled, f.shared_wide);
     s2.obuf = sbuf;
     (void)bytes_is;
-    if (!ok(launch_fc(s2, false, f.shared_tiled))) return MOE_ERR_HIP;
+    if (!ok(launch_fc(s2, false, f.shared_tiled, f.shared_wide))) return MOE_ERR_HIP;
   }
   // 8. y = bf16(accumulator)
   if (!mark(MOE_STAGE_FINALIZE)) return MOE_ERR_HIP;

@@ -31,6 +31,9 @@ CASES = {
     "w4a8_stream_items": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=512, H=2048, I=1024, E=32, k=4),
     "w6a8_stream_items": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=512, H=2048, I=1024, E=32, k=4,
                                     I_shared=1024),
+    # MXFP8 activations x E2M1 with H not a multiple of 256: the 32x32 tiled
+    # kernel instead of the wide one
+    "w4a8_h384": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=200, H=384, I=256, E=4, k=2),
     # bf16 activations with I not a multiple of 256: the 16-row stream kernels
     "w4a16_k384": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=40, H=384, I=384, E=8, k=2),
 }
