@@ -35,8 +35,9 @@ struct FcArgs {
   // outputs
   void* out;           // FC1: h (bf16 [P, I] or E4M3 codes [P, I])
   uint8_t* out_scale;  // FC1 MX: h scales [P, I/32]
-  float* obuf;         // FC2: fp32 rows [A, N] (routed: row = assignment a, holding
-                       // w(a) * o; dense: row = token, holding dense_weight * o)
+  uint16_t* obuf;      // FC2: bf16 rows [A, N] (routed: row = assignment a, holding
+                       // w(a) * o; dense: row = token, holding dense_weight * o),
+                       // the product taken in fp32 and rounded once (RNE)
 };
 
 // Columns of N covered by one wave of the stream kernels.

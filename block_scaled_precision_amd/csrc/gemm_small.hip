@@ -202,9 +202,9 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (4 * g + i < it.rows) {
-          float* o = p.obuf + (int64_t)orow[i] * p.N + it.nb * SBN + 32 * w + r16;
-          o[0] = wt[i] * acc[0][i];
-          o[16] = wt[i] * acc[1][i];
+          uint16_t* o = p.obuf + (int64_t)orow[i] * p.N + it.nb * SBN + 32 * w + r16;
+          o[0] = f32_to_bf16_rne(wt[i] * acc[0][i]);
+          o[16] = f32_to_bf16_rne(wt[i] * acc[1][i]);
         }
       }
     }

@@ -277,9 +277,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       orow = a;
       w = p.topk_w[a];
     }
-    float* o = p.obuf + orow * H + col0 + r;
+    uint16_t* o = p.obuf + orow * H + col0 + r;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) o[16 * n] = w * acc[n][i];
+    for (int n = 0; n < NB; ++n) o[16 * n] = f32_to_bf16_rne(w * acc[n][i]);
   }
 }
 

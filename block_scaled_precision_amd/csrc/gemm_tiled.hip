@@ -320,9 +320,9 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
             orow = tsrc[row];
             w = twt[row];
           }
-          float* o = p.obuf + orow * p.N + it.nb * TBN + 64 * wn + l32;
-          o[0] = w * acc[m][0][i];
-          o[32] = w * acc[m][1][i];
+          uint16_t* o = p.obuf + orow * p.N + it.nb * TBN + 64 * wn + l32;
+          o[0] = f32_to_bf16_rne(w * acc[m][0][i]);
+          o[32] = f32_to_bf16_rne(w * acc[m][1][i]);
         }
       }
     }

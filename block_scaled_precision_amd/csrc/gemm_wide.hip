@@ -511,9 +511,9 @@ __device__ __forceinline__ void wave_main(const FcArgs& p, const Sched& sc, uint
             orow = tsrc[row];
             wt = twt[row];
           }
-          float* out = p.obuf + orow * p.N + it.nb * TBN + 128 * wn + l16;
+          uint16_t* out = p.obuf + orow * p.N + it.nb * TBN + 128 * wn + l16;
 #pragma unroll
-          for (int n = 0; n < kTiles; ++n) out[16 * n] = wt * acc[m][n][i];
+          for (int n = 0; n < kTiles; ++n) out[16 * n] = f32_to_bf16_rne(wt * acc[m][n][i]);
         }
       }
     }

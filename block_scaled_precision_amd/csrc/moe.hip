@@ -58,30 +58,50 @@ static int device_cus() {
 // Unpermute-combine (TokenSpeed SiTU page, "Supported contract": the layer
 // output is the routing-weighted sum over the selected experts; mxfp6-sm120
 // page, "Routed MoE": routed/shared reduction).  obuf row t*k + j holds
-// w[t,j] * FC2 output of assignment (t, j) in fp32; sbuf row t the weighted
-// shared-expert output (or nullptr).  y[t] = bf16 RNE of the sum over the
-// assignments whose expert lies in the local range [off, off + L) (rows of
-// other experts were never written), added in slot order, plus sbuf[t].
-__global__ __launch_bounds__(256) void k_combine(const float4* __restrict__ obuf, const float4* __restrict__ sbuf,
+// w[t,j] * FC2 output of assignment (t, j) rounded to bf16; sbuf row t the
+// weighted shared-expert output (or nullptr), likewise.  y[t] = bf16 RNE of the
+// fp32 sum over the assignments whose expert lies in the local range
+// [off, off + L) (rows of other experts were never written), added in slot
+// order, plus sbuf[t].  Each thread takes 8 columns (16 bytes per row) and
+// issues the loads of up to 4 slots before adding them: the rows of slots
+// whose expert is not local are loaded too (they lie in the workspace) and
+// dropped.
+__device__ __forceinline__ void add_bf16x8(float (&s)[8], uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    s[2 * q] += __uint_as_float(w[q] << 16);
+    s[2 * q + 1] += __uint_as_float(w[q] & 0xffff0000u);
+  }
+}
+__global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ obuf, const uint4* __restrict__ sbuf,
                                                  const int32_t* __restrict__ ids, int k, int off, int L,
-                                                 int H4, int64_t n4, uint2* __restrict__ y) {
+                                                 int H8, int64_t n8, uint4* __restrict__ y) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const int64_t t = i / H4;
-    const int64_t c = i - t * H4;
-    float4 s = sbuf ? sbuf[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int e = ids[t * k + j] - off;
-      if (e < 0 || e >= L) continue;
-      const float4 v = obuf[(t * k + j) * H4 + c];
-      s.x += v.x;
-      s.y += v.y;
-      s.z += v.z;
-      s.w += v.w;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const int64_t t = i / H8;
+    const int64_t c = i - t * H8;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      uint4 v[4];
+      bool use[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = j0 + q < k ? j0 + q : j0;
+        const int e = ids[t * k + j] - off;
+        use[q] = j0 + q < k && e >= 0 && e < L;
+        v[q] = obuf[(t * k + j) * H8 + c];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (use[q]) add_bf16x8(s, v[q]);
     }
-    const uint32_t lo = (uint32_t)f32_to_bf16_rne(s.x) | ((uint32_t)f32_to_bf16_rne(s.y) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16_rne(s.z) | ((uint32_t)f32_to_bf16_rne(s.w) << 16);
-    y[i] = make_uint2(lo, hi);
+    if (sbuf) add_bf16x8(s, sbuf[i]);
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = (uint32_t)f32_to_bf16_rne(s[2 * q]) | ((uint32_t)f32_to_bf16_rne(s[2 * q + 1]) << 16);
+    y[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
@@ -158,8 +178,8 @@ static FusedPlan plan(const moe_problem_t& p) {
   f.hsc = mx ? take(f.A * I / 32) : 0;
   f.hs = Is ? take(T * Is * (mx ? 1 : 2)) : 0;
   f.hssc = (Is && mx) ? take(T * Is / 32) : 0;
-  f.obuf = take(f.A * H * 4);
-  f.sbuf = Is ? take(T * H * 4) : 0;
+  f.obuf = take(f.A * H * 2);
+  f.sbuf = Is ? take(T * H * 2) : 0;
   f.total = o;
   return f;
 }
@@ -283,8 +303,8 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   const bool mx = p->act == MOE_ACT_MXFP8;
   const int wf = p->w_fmt == MX_E2M1 ? 1 : 2;
   const int T = p->T, H = p->H, I = p->I, k = p->k, Is = p->I_shared;
-  float* obuf = (float*)(ws + f.obuf);
-  float* sbuf = Is ? (float*)(ws + f.sbuf) : nullptr;
+  uint16_t* obuf = (uint16_t*)(ws + f.obuf);
+  uint16_t* sbuf = Is ? (uint16_t*)(ws + f.sbuf) : nullptr;
   hipError_t e = hipSuccess;
   auto ok = [&](hipError_t r) {
     if (r != hipSuccess && e == hipSuccess) e = r;
@@ -417,9 +437,9 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   }
   // 8. y = bf16(accumulator)
   if (!mark(MOE_STAGE_FINALIZE)) return MOE_ERR_HIP;
-  const int64_t n4 = (int64_t)T * H / 4;
-  k_combine<<<grid_for(n4, 256, 16384), 256, 0, stream>>>((const float4*)obuf, (const float4*)sbuf, ids, k, f.off,
-                                                          f.L, H / 4, n4, (uint2*)t->y);
+  const int64_t n8 = (int64_t)T * H / 8;
+  k_combine<<<grid_for(n8, 256, 16384), 256, 0, stream>>>((const uint4*)obuf, (const uint4*)sbuf, ids, k, f.off,
+                                                          f.L, H / 8, n8, (uint4*)t->y);
   if (!ok(hipGetLastError())) return MOE_ERR_HIP;
   if (!mark(MOE_NUM_STAGES)) return MOE_ERR_HIP;
   return MOE_OK;

@@ -183,9 +183,10 @@ enum {
  * and y is that shard's partial output (the caller sums shards); the shared
  * expert, if any, is added by every call.
  * Precision: FC products accumulate in fp32; each expert's output row is
- * scaled by its routing weight in fp32; y is one bf16 rounding of the fp32 sum
- * of those rows taken in slot order j = 0..k-1, then the shared expert's
- * (results are deterministic from run to run).
+ * scaled by its routing weight in fp32 and rounded to bf16 (RNE); y is one
+ * bf16 rounding of the fp32 sum of those rows taken in slot order
+ * j = 0..k-1, then the shared expert's row (scaled and rounded the same way);
+ * results are deterministic from run to run.
  * Workspace: at least moe_fused_workspace_bytes(p) bytes, 256-byte aligned.
  */
 size_t moe_fused_workspace_bytes(const moe_problem_t* p);
