@@ -17,6 +17,8 @@ struct FcArgs {
   // routed rows: permuted position p -> assignment a = t*k + j
   const int32_t* sorted_assign;
   int k;
+  uint32_t kdiv;       // k > 1: ceil(2^32 / k), so that the token of assignment a is
+                       // umulhi(a, kdiv), exact while a*k < 2^32
   const float* topk_w;  // FC2 routed: weight of assignment a
   const float* sorted_w;  // routed: weight of permuted row p (= topk_w[sorted_assign[p]])
   float dense_weight;   // FC2 dense: weight of every row

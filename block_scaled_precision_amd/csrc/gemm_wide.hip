@@ -70,35 +70,39 @@ constexpr int kSubs = TBM / 16 / 4;  // 16-row sub-blocks per wave
 constexpr int kTiles = TBN / 2 / 16; // column tiles per wave
 static_assert(TBM == 192 && TBN == 256, "copy maps below assume 192 x 256 items");
 
-// LDS layout: [A ring: 3 x (codes TBM x 128 B + scale words TBM x 4 B)]
-//             [B ring: 4 x (codes TBN x 64 B + scale words TBN x 4 B)]
+// LDS layout: [A ring: 3 x codes TBM x 128 B] [B ring: 4 x codes TBN x 64 B]
+//             [A scale groups: 2 x TBM x 16 B] [B scale groups: 2 x TBN x 16 B]
 //             [row tables: 4 x (source row TBM x 4 B + weight TBM x 4 B)]
+// Scales travel in groups of 4 K-steps: a row's 16 scale bytes for 4
+// consecutive steps are contiguous in both operands, so one 16-byte copy per
+// row serves 4 steps (per-step 4-byte copies cost as many memory requests as
+// the codes themselves).
 constexpr int kAStages = 3;
 constexpr int kBStages = 4;
 constexpr int kTables = 4;
+constexpr int kGroup = 4;  // K-steps per scale group
 // The row table of item i+1 is copied when item i's first stage is copied,
 // kAStages steps before item i starts, into the buffer of item i+1-kTables,
 // whose last reader is its epilogue at the end of item i+2-kTables: with items
 // of at least 2 steps the copy comes after that epilogue.
 static_assert((kTables - 2) * 2 >= kAStages, "row table ring too short");
-constexpr int A_CODES = TBM * TBK;
-constexpr int A_STAGE = A_CODES + TBM * 4;
+constexpr int A_STAGE = TBM * TBK;
 constexpr int B_ROW = TBK / 2;  // bytes of one E2M1 weight row per step
-constexpr int B_CODES = TBN * B_ROW;
-constexpr int B_STAGE = B_CODES + TBN * 4;
+constexpr int B_STAGE = TBN * B_ROW;
+constexpr int AS_GROUP = TBM * 4 * kGroup;
+constexpr int BS_GROUP = TBN * 4 * kGroup;
 constexpr int TABLE = TBM * 8;
 constexpr int L_A = 0;
 constexpr int L_B = L_A + kAStages * A_STAGE;
-constexpr int L_TBL = L_B + kBStages * B_STAGE;
+constexpr int L_AS = L_B + kBStages * B_STAGE;
+constexpr int L_BS = L_AS + 2 * AS_GROUP;
+constexpr int L_TBL = L_BS + 2 * BS_GROUP;
 constexpr int L_TOTAL = L_TBL + kTables * TABLE;
 static_assert(L_TOTAL <= 160 * 1024, "LDS");
 
-// copies per wave and stage: activation waves 6 x 1 KB of codes + one 256-B
-// copy of scale words; weight waves 4 x 1 KB + one 256-B copy of scale words
-constexpr int kACodeCopies = A_CODES / 1024 / 4;
-constexpr int kACopies = kACodeCopies + 1;
-constexpr int kBCodeCopies = B_CODES / 1024 / 4;
-constexpr int kBCopies = kBCodeCopies + 1;
+// 1-KB code copies per wave and stage
+constexpr int kACodeCopies = A_STAGE / 1024 / 4;
+constexpr int kBCodeCopies = B_STAGE / 1024 / 4;
 
 // A tile: row r holds 8 chunks of 16 B; chunk c sits at slot c ^ (r & 7), so
 // that 8 consecutive rows read at the same k land in 8 different bank groups.
@@ -106,21 +110,6 @@ __device__ __forceinline__ int a_off(int r, int c) { return r * TBK + 16 * (c ^ 
 // B tile: row r holds 4 chunks of 16 B; chunk c sits at slot c ^ ((r >> 1) & 3)
 // (rows are 64 B, so rows r and r+2 would otherwise share banks).
 __device__ __forceinline__ int b_off(int r, int c) { return r * B_ROW + 16 * (c ^ ((r >> 1) & 3)); }
-
-// at most n (<= N) stages of COPIES copies each may stay in flight (copies
-// issued before them, such as row tables, are waited for as well)
-template <int COPIES, int N>
-__device__ __forceinline__ void wait_stages(int n) {
-  if constexpr (N > 0) {
-    if (n >= N) {
-      wait_vm_lgkm0<N * COPIES>();
-      return;
-    }
-    wait_stages<COPIES, N - 1>(n);
-  } else {
-    wait_vm_lgkm0<0>();
-  }
-}
 
 struct ItemGeom {
   int expert, p0, rows, nb;
@@ -159,15 +148,12 @@ __device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, const Sched& sc, 
   return g;
 }
 
-// K step copied at step ls of an item.  The N-blocks of one M-tile run at the
-// same time on one XCD and read the same activation rows; starting each at a
-// different K step (rotated by its N-block index) means only the first to
-// reach a step misses in L2 and the others hit, instead of all of them waiting
-// on the same miss.  The multiply is indifferent to the K order.
-__device__ __forceinline__ int k_step(const Sched& sc, int nb, int ls) {
-  const int k = ls + nb * sc.nk / sc.NB;
-  return k < sc.nk ? k : k - sc.nk;
-}
+// K step copied at step ls of an item: the steps run in K order, so the
+// N-blocks of one M-tile, which run together on one XCD, read each activation
+// stage at about the same time and one L2 fill serves them all.  (Starting
+// each N-block at a different K step, which spreads the misses, measured
+// slower with 256-row blocks and grouped scale copies.)
+__device__ __forceinline__ int k_step(const Sched&, int, int ls) { return ls; }
 
 // weight row held at B-tile row jr.  FC1: each half of the block (the rows of
 // one wave) is 64 gate rows then the 64 matching up rows, so a wave holds both
@@ -201,120 +187,180 @@ __device__ __forceinline__ void copy_table(const FcArgs& p, const ItemGeom& it, 
   }
 }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n in [LO, HI] (binary search
+// over the immediate forms; n above HI waits for HI, which is stricter).
+template <int LO, int HI>
+__device__ __forceinline__ void wait_ops(int n) {
+  if constexpr (LO == HI) {
+    wait_vm_lgkm0<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_ops<MID, HI>(n);
+    else wait_ops<LO, MID - 1>(n);
+  }
+}
+
+// Memory-counter bookkeeping of a copy stream in closed form.  A wave issues
+// its prologue (code stages 0..NS-1, C copies each, then scale groups 0 and
+// 1, one copy each) and after barrier g the code stage of step g+NS and, when
+// g % 4 == 3, scale group (g+1)/4 + 1.  Row-table copies are left out of the
+// count: they only add to the copies in flight after a given one, so leaving
+// them out makes a wait stricter, never looser; stages or groups past the end
+// are left out of the issue but not of the count, which again only makes the
+// waits stricter.
+template <int NS, int C>
+struct CopyCount {
+  static constexpr int P = NS * C + 2;
+  // copies issued before barrier g
+  static __device__ __forceinline__ int before(int g) { return P + g * C + g / kGroup; }
+  // copies issued up to and including code stage s / scale group G
+  static __device__ __forceinline__ int code_end(int s) {
+    return s < NS ? (s + 1) * C : P + (s - NS + 1) * C + (s - NS) / kGroup;
+  }
+  static __device__ __forceinline__ int group_end(int G) {
+    return G < 2 ? NS * C + G + 1 : P + (kGroup * G - kGroup) * C + (G - 2) + 1;
+  }
+  // before barrier g: the code stage of step g+1 has landed and, when step g+1
+  // opens a scale group, that group too
+  static __device__ __forceinline__ void wait_step(int g) {
+    int need = code_end(g + 1);
+    if (((g + 1) & (kGroup - 1)) == 0) need = max(need, group_end((g + 1) / kGroup));
+    wait_ops<0, NS * C + 2>(before(g) - need);
+  }
+};
+
 // The activation stream of wave (wm, 0): codes of rows [48 wm, 48 wm + 48)
 // (1-KB copy t = 6 wm + i holds rows 8t .. 8t+7, lane -> row 8t + lane/8,
-// slot lane%8 receiving chunk (lane%8) ^ (row%8)), scale words of rows
-// 64 min(wm, 2) + lane, and the row tables.
+// slot lane%8 receiving chunk (lane%8) ^ (row%8)), scale groups of rows
+// 64 min(wm, 2) + lane (16 bytes per row: the 4 K-steps of the group), and
+// the row tables.  A row table is read only after the per-step waits have
+// covered the copy that wrote it: the table of item i goes out before item
+// i-1's first code stage, which every wait from step nk*i - nk + 1 on includes.
 template <bool FC1>
 struct ACopier {
+  using Count = CopyCount<kAStages, kACodeCopies>;
   uint32_t src[kACodeCopies];  // byte offsets into the activations (< 4 GiB)
-  uint32_t ssrc;               // byte offset into the activation scales
-  int li, ls, issued, nb;
+  int nb;                      // N-block of the code cursor's item
 
-  __device__ __forceinline__ void setup(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm) {
-    const int lane = threadIdx.x & 63;
-    const ItemGeom it = item_geom(p, sc, li);
-    nb = it.nb;
-    const bool routed = p.dense_rows == 0;
+  // activation row (token for FC1, permuted row for FC2) of tile row r of item li
+  __device__ __forceinline__ static uint32_t src_row(const FcArgs& p, const uint8_t* smem, const ItemGeom& it,
+                                                     int li, int r) {
+    r = r < it.rows ? r : it.rows - 1;  // rows past the tile repeat its last row
+    if (p.dense_rows > 0) return (uint32_t)(it.p0 + r);
     const int32_t* tsrc = (const int32_t*)(smem + L_TBL + (li % kTables) * TABLE);
-    auto src_row = [&](int r) -> uint32_t {
-      r = r < it.rows ? r : it.rows - 1;  // rows past the tile repeat its last row
-      if (!routed) return (uint32_t)(it.p0 + r);
-      return (uint32_t)(FC1 ? tsrc[r] / p.k : it.p0 + r);
-    };
-    const int c = (lane & 7) ^ (lane >> 3);
-#pragma unroll
-    for (int i = 0; i < kACodeCopies; ++i)
-      src[i] = src_row(8 * (kACodeCopies * wm + i) + (lane >> 3)) * (uint32_t)p.K + 16 * c;
-    ssrc = src_row(64 * min(wm, 2) + lane) * (uint32_t)(p.K / 32);
+    if (!FC1) return (uint32_t)(it.p0 + r);
+    return p.k == 1 ? (uint32_t)tsrc[r] : __umulhi((uint32_t)tsrc[r], p.kdiv);
   }
 
-  // copies the next stage into buffer issued % kAStages
-  __device__ __forceinline__ void issue(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm) {
-    if (issued >= sc.total) return;
+  // code stage of step s
+  __device__ __forceinline__ void issue_code(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int s) {
+    if (s >= sc.total) return;
+    const int lane = threadIdx.x & 63;
     const uint32_t lds0 = lds_addr(smem);
-    const bool routed = p.dense_rows == 0;
+    const int li = s / sc.nk, ls = s - li * sc.nk;
     if (ls == 0) {
-      // the next item's table goes out before this item's first stage; this
-      // item's table went out before the previous item's stages
-      if (routed && li + 1 < sc.my_items)
+      // the next item's table goes out before this item's first stage
+      if (p.dense_rows == 0 && li + 1 < sc.my_items)
         copy_table(p, item_geom(p, sc, li + 1), lds0 + L_TBL + ((li + 1) % kTables) * TABLE, wm == 0);
-      if (routed && li > 0) wait_stages<kACopies, kAStages - 1>(sc.nk);
-      setup(p, sc, smem, wm);
+      const ItemGeom it = item_geom(p, sc, li);
+      nb = it.nb;
+      const int c = (lane & 7) ^ (lane >> 3);
+#pragma unroll
+      for (int i = 0; i < kACodeCopies; ++i)
+        src[i] = src_row(p, smem, it, li, 8 * (kACodeCopies * wm + i) + (lane >> 3)) * (uint32_t)p.K + 16 * c;
     }
     const int ks = k_step(sc, nb, ls);
     const uint8_t* a = (const uint8_t*)p.a + ks * TBK;
-    const uint32_t base = lds0 + L_A + (issued % kAStages) * A_STAGE;
+    const uint32_t base = lds0 + L_A + (s % kAStages) * A_STAGE;
 #pragma unroll
     for (int i = 0; i < kACodeCopies; ++i) lds_copy16_s(a, src[i], base + 1024 * (kACodeCopies * wm + i));
-    lds_copy4_s(p.a_scale + 4 * ks, ssrc, base + A_CODES + 256 * min(wm, 2));
-    ++issued;
-    if (++ls == sc.nk) {
-      ls = 0;
-      ++li;
-    }
+  }
+
+  // scale group G (steps 4G .. 4G+3)
+  __device__ __forceinline__ void issue_group(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int G) {
+    if (kGroup * G >= sc.total) return;
+    const int lane = threadIdx.x & 63;
+    const int li = kGroup * G / sc.nk, ls = kGroup * G - li * sc.nk;
+    const ItemGeom it = item_geom(p, sc, li);
+    const int u = min(wm, TBM / 64 - 1);
+    const uint32_t off = src_row(p, smem, it, li, 64 * u + lane) * (uint32_t)(p.K / 32);
+    lds_copy16_s(p.a_scale + 4 * k_step(sc, it.nb, ls), off,
+                 lds_addr(smem) + L_AS + (G % 2) * AS_GROUP + 1024 * u);
   }
 
   __device__ __forceinline__ void prologue(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm) {
-    li = ls = issued = 0;
     if (p.dense_rows == 0) {
       copy_table(p, item_geom(p, sc, 0), lds_addr(smem) + L_TBL, wm == 0);
       wait_vm_lgkm0<0>();
     }
-    for (int s = 0; s < kAStages; ++s) issue(p, sc, smem, wm);
+    for (int s = 0; s < kAStages; ++s) issue_code(p, sc, smem, wm, s);
+    issue_group(p, sc, smem, wm, 0);
+    issue_group(p, sc, smem, wm, 1);
   }
-  // stage s has landed once at most the stages issued after it remain
-  __device__ __forceinline__ void wait_for(int s) { wait_stages<kACopies, kAStages - 1>(issued - 1 - s); }
+  // after barrier g
+  __device__ __forceinline__ void issue(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int g) {
+    issue_code(p, sc, smem, wm, g + kAStages);
+    if ((g & (kGroup - 1)) == kGroup - 1) issue_group(p, sc, smem, wm, (g + 1) / kGroup + 1);
+  }
+  __device__ __forceinline__ void wait_for(int g) { Count::wait_step(g); }
 };
 
 // The weight stream of wave (wm, 1): codes of B-tile rows [64 wm, 64 wm + 64)
-// (1-KB copy t = 4 wm + i holds rows 16t .. 16t+15) and scale words of rows
+// (1-KB copy t = 4 wm + i holds rows 16t .. 16t+15) and scale groups of rows
 // 64 wm + lane.
 template <bool FC1>
 struct BCopier {
-  int li, ls, issued, nb, expert;  // wave-uniform; the per-lane parts of the
-                                   // offsets are recomputed at each issue
+  using Count = CopyCount<kBStages, kBCodeCopies>;
+  int nb, expert;  // of the code cursor's item; per-lane offsets are recomputed at each issue
 
   // First weight row of the wave's 64 B-tile rows [64 wm, 64 wm + 64): FC1 takes
   // gate rows (even wm) or the matching up rows (odd wm) of h columns
   // nb*128 + 64 (wm/2) + [0, 64); FC2 takes output rows nb*256 + 64 wm + [0, 64).
-  __device__ __forceinline__ int64_t row0(const FcArgs& p, int wm) const {
-    if (FC1) return (int64_t)nb * (TBN / 2) + 64 * (wm >> 1) + ((wm & 1) ? (int64_t)p.N : 0);
-    return (int64_t)nb * TBN + 64 * wm;
+  __device__ __forceinline__ static int64_t row0(const FcArgs& p, int nb_, int wm) {
+    if (FC1) return (int64_t)nb_ * (TBN / 2) + 64 * (wm >> 1) + ((wm & 1) ? (int64_t)p.N : 0);
+    return (int64_t)nb_ * TBN + 64 * wm;
   }
 
-  __device__ __forceinline__ void issue(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm) {
-    if (issued >= sc.total) return;
+  __device__ __forceinline__ void issue_code(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int s) {
+    if (s >= sc.total) return;
     const int lane = threadIdx.x & 63;
+    const int li = s / sc.nk, ls = s - li * sc.nk;
     if (ls == 0) {
       const ItemGeom it = item_geom(p, sc, li);
       nb = it.nb;
       expert = it.expert;
     }
     const int ks = k_step(sc, nb, ls);
-    const int64_t r0 = row0(p, wm);
-    const uint8_t* w = p.w + (int64_t)expert * p.w_estride + r0 * (p.K / 2) + ks * B_ROW;
-    const uint8_t* sw = p.w_scale + (int64_t)expert * p.ws_estride + r0 * (p.K / 32) + 4 * ks;
+    const uint8_t* w = p.w + (int64_t)expert * p.w_estride + row0(p, nb, wm) * (p.K / 2) + ks * B_ROW;
     // copy i: rows 16i + lane/4 of the wave's 64, slot lane%4 receiving chunk
     // (lane%4) ^ ((row/2)%4) = (lane%4) ^ ((lane/8)%4)
     const uint32_t lo = (uint32_t)(lane >> 2) * (uint32_t)(p.K / 2) + 16 * ((lane & 3) ^ ((lane >> 3) & 3));
-    const uint32_t base = lds_addr(smem) + L_B + (issued % kBStages) * B_STAGE;
+    const uint32_t base = lds_addr(smem) + L_B + (s % kBStages) * B_STAGE;
 #pragma unroll
     for (int i = 0; i < kBCodeCopies; ++i)
       lds_copy16_s(w, lo + (uint32_t)(16 * i) * (uint32_t)(p.K / 2), base + 1024 * (kBCodeCopies * wm + i));
-    lds_copy4_s(sw, (uint32_t)lane * (uint32_t)(p.K / 32), base + B_CODES + 256 * wm);
-    ++issued;
-    if (++ls == sc.nk) {
-      ls = 0;
-      ++li;
-    }
+  }
+
+  __device__ __forceinline__ void issue_group(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int G) {
+    if (kGroup * G >= sc.total) return;
+    const int lane = threadIdx.x & 63;
+    const int li = kGroup * G / sc.nk, ls = kGroup * G - li * sc.nk;
+    const ItemGeom it = item_geom(p, sc, li);
+    const uint8_t* sw =
+        p.w_scale + (int64_t)it.expert * p.ws_estride + row0(p, it.nb, wm) * (p.K / 32) + 4 * k_step(sc, it.nb, ls);
+    lds_copy16_s(sw, (uint32_t)lane * (uint32_t)(p.K / 32), lds_addr(smem) + L_BS + (G % 2) * BS_GROUP + 1024 * wm);
   }
 
   __device__ __forceinline__ void prologue(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm) {
-    li = ls = issued = 0;
-    for (int s = 0; s < kBStages; ++s) issue(p, sc, smem, wm);
+    for (int s = 0; s < kBStages; ++s) issue_code(p, sc, smem, wm, s);
+    issue_group(p, sc, smem, wm, 0);
+    issue_group(p, sc, smem, wm, 1);
   }
-  __device__ __forceinline__ void wait_for(int s) { wait_stages<kBCopies, kBStages - 1>(issued - 1 - s); }
+  __device__ __forceinline__ void issue(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int g) {
+    issue_code(p, sc, smem, wm, g + kBStages);
+    if ((g & (kGroup - 1)) == kGroup - 1) issue_group(p, sc, smem, wm, (g + 1) / kGroup + 1);
+  }
+  __device__ __forceinline__ void wait_for(int g) { Count::wait_step(g); }
 };
 
 // ------------------------------------------------------------ epilogue ---
@@ -361,7 +407,7 @@ struct Frags {
 // this offset plus a compile-time constant (sub-block and column-tile offsets
 // are multiples of 8 rows and leave the swizzles unchanged).
 struct LaneOffs {
-  int a_lo, a_hi, a_sc, b, b_sc;
+  int a_lo, a_hi, a_sc, b, b_sc;  // a_sc, b_sc: in a scale group buffer
 };
 __device__ __forceinline__ LaneOffs lane_offs(int wm, int wn) {
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
@@ -369,23 +415,26 @@ __device__ __forceinline__ LaneOffs lane_offs(int wm, int wn) {
   LaneOffs o;
   o.a_lo = a_off(r, g);
   o.a_hi = a_off(r, 4 + g);
-  o.a_sc = A_CODES + 4 * r + g;
+  o.a_sc = 4 * kGroup * r + g;
   o.b = b_off(jr, g);
-  o.b_sc = B_CODES + 4 * jr + g;
+  o.b_sc = 4 * kGroup * jr + g;
   return o;
 }
 
-// A sub-block m (rows 16 (wm + 4m) + l16), B column tile n (rows 128 wn + 16n + l16).
-__device__ __forceinline__ void read_a(const uint8_t* as, const LaneOffs& o, int m, v8i& a, int& sc) {
+// A sub-block m (rows 16 (wm + 4m) + l16), B column tile n (rows 128 wn + 16n + l16);
+// `ass` / `bss` point at the step's scale words in its scale group buffer.
+__device__ __forceinline__ void read_a(const uint8_t* as, const uint8_t* ass, const LaneOffs& o, int m, v8i& a,
+                                       int& sc) {
   const int mo = 64 * m * TBK;
   const v4i lo = *(const v4i*)(as + o.a_lo + mo);
   const v4i hi = *(const v4i*)(as + o.a_hi + mo);
   a = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  sc = *(const uint8_t*)(as + o.a_sc + 4 * 64 * m);
+  sc = *(const uint8_t*)(ass + o.a_sc + 4 * kGroup * 64 * m);
 }
-__device__ __forceinline__ void read_b(const uint8_t* bs, const LaneOffs& o, int n, v4i& b, int& sc) {
+__device__ __forceinline__ void read_b(const uint8_t* bs, const uint8_t* bss, const LaneOffs& o, int n, v4i& b,
+                                       int& sc) {
   b = *(const v4i*)(bs + o.b + 16 * n * B_ROW);
-  sc = *(const uint8_t*)(bs + o.b_sc + 4 * 16 * n);
+  sc = *(const uint8_t*)(bss + o.b_sc + 4 * kGroup * 16 * n);
 }
 
 // One K-step for a wave holding NM (0 to kSubs) sub-blocks: the MFMAs of the
@@ -395,15 +444,15 @@ __device__ __forceinline__ void read_b(const uint8_t* bs, const LaneOffs& o, int
 // MFMA with the last column tile.
 template <int NM>
 __device__ __forceinline__ void mul_step(v4f (&acc)[kSubs][kTiles], Frags& f, const uint8_t* nas, const uint8_t* nbs,
-                                         const LaneOffs& o) {
+                                         const uint8_t* nass, const uint8_t* nbss, const LaneOffs& o) {
 #pragma unroll
   for (int n = 0; n < kTiles; ++n) {
 #pragma unroll
     for (int m = 0; m < kSubs; ++m) {
       if (m < NM) acc[m][n] = mfma16_f8_f4_w(f.a[m], f.b[n], acc[m][n], 0, Fmt<1>::MFMA, 0, f.asc[m], 0, f.bsc[n]);
-      if (n == kTiles - 1) read_a(nas, o, m, f.a[m], f.asc[m]);
+      if (n == kTiles - 1) read_a(nas, nass, o, m, f.a[m], f.asc[m]);
     }
-    read_b(nbs, o, n, f.b[n], f.bsc[n]);
+    read_b(nbs, nbss, o, n, f.b[n], f.bsc[n]);
     // keep this order: the scheduler would otherwise hoist every read above
     // the MFMAs and need second register sets
     __builtin_amdgcn_sched_barrier(0);
@@ -411,22 +460,25 @@ __device__ __forceinline__ void mul_step(v4f (&acc)[kSubs][kTiles], Frags& f, co
 }
 
 // The nk steps of one item for a wave holding NM sub-blocks, from global step
-// gbase.  Before barrier g the wave's own stage of step g+1 has landed and its
-// reads of step g's stages are complete; after it, the wave copies its next
-// stage into the buffer step g used and multiplies step g while reading step
-// g+1's fragments (past the last step the reads hit a stale buffer and go
-// unused).
+// gbase.  Before barrier g the wave's own copies for step g+1 (code stage and,
+// at a group start, scale group) have landed and its reads of step g's data
+// are complete; after it, the wave copies its next stage into the buffer step g
+// used (and, after a group's last step, the group after next into that group's
+// buffer) and multiplies step g while reading step g+1's fragments (past the
+// last step the reads hit a stale buffer and go unused).
 template <int NM, class Copier>
 __device__ __forceinline__ void item_steps(const FcArgs& p, const Sched& sc, v4f (&acc)[kSubs][kTiles], Frags& f,
                                            const LaneOffs& o, uint8_t* smem, Copier& cp, int wm, int gbase) {
   for (int s = 0; s < sc.nk; ++s) {
     const int g = gbase + s;
-    if (g + 1 < sc.total) cp.wait_for(g + 1);
+    if (g + 1 < sc.total) cp.wait_for(g);
     else wait_lgkm0();
     barrier();
-    cp.issue(p, sc, smem, wm);
+    cp.issue(p, sc, smem, wm, g);
     const int nx = g + 1;
-    mul_step<NM>(acc, f, smem + L_A + (nx % kAStages) * A_STAGE, smem + L_B + (nx % kBStages) * B_STAGE, o);
+    const int grp = (nx / kGroup) & 1, q = nx & (kGroup - 1);
+    mul_step<NM>(acc, f, smem + L_A + (nx % kAStages) * A_STAGE, smem + L_B + (nx % kBStages) * B_STAGE,
+                 smem + L_AS + grp * AS_GROUP + 4 * q, smem + L_BS + grp * BS_GROUP + 4 * q, o);
   }
 }
 
@@ -451,12 +503,12 @@ __device__ __forceinline__ void wave_main(const FcArgs& p, const Sched& sc, uint
   // step 0's fragments: its stages have landed at the first barrier
   Frags f;
   const LaneOffs o = lane_offs(wm, wn);
-  cp.wait_for(0);
+  wait_vm_lgkm0<0>();
   barrier();
 #pragma unroll
-  for (int n = 0; n < kTiles; ++n) read_b(smem + L_B, o, n, f.b[n], f.bsc[n]);
+  for (int n = 0; n < kTiles; ++n) read_b(smem + L_B, smem + L_BS, o, n, f.b[n], f.bsc[n]);
 #pragma unroll
-  for (int m = 0; m < kSubs; ++m) read_a(smem + L_A, o, m, f.a[m], f.asc[m]);
+  for (int m = 0; m < kSubs; ++m) read_a(smem + L_A, smem + L_AS, o, m, f.a[m], f.asc[m]);
 
   int gbase = 0;
   for (int ci = 0; ci < sc.my_items; ++ci) {

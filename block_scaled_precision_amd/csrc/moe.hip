@@ -151,8 +151,12 @@ static FusedPlan plan(const moe_problem_t& p) {
             p.I >= kTiledMinK;
   f.shared_tiled = mxa && p.T >= kTiledMinRowsPerExpert && p.H >= kTiledMinK && p.I_shared >= kTiledMinK;
   // E2M1 weights take the wide tiled kernel (256-row weight blocks)
-  f.wide = f.tiled && p.w_fmt == MX_E2M1 && p.H % kWideCols == 0;
-  f.shared_wide = f.shared_tiled && p.w_fmt == MX_E2M1 && p.H % kWideCols == 0;
+  // (K a multiple of 512 and at least 1024: scale groups of 4 K-steps, items of
+  // at least 8 steps; A*k < 2^32: tokens from assignment ids by multiplication)
+  const bool wide_k = p.H % 512 == 0 && p.I % 512 == 0 && p.H >= 1024 && p.I >= 1024;
+  f.wide = f.tiled && p.w_fmt == MX_E2M1 && wide_k && (double)f.A * p.k < 4294967296.0;
+  f.shared_wide = f.shared_tiled && p.w_fmt == MX_E2M1 && p.H % 512 == 0 && p.H >= 1024 &&
+                  p.I_shared % 512 == 0 && p.I_shared >= 1024;
   f.bm = f.tiled ? kTiledRows : kStreamRows;
   f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
@@ -360,6 +364,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.dense_rows = 0;
   a1.sorted_assign = sorted;
   a1.k = k;
+  a1.kdiv = k > 1 ? (uint32_t)(((1ull << 32) + k - 1) / k) : 0u;  // unused for k = 1
   a1.topk_w = wts;
   a1.sorted_w = sorted_w;
   a1.a = mx ? (const void*)xq : t->x;

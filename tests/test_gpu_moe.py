@@ -31,6 +31,9 @@ CASES = {
     "w4a8_stream_items": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=512, H=2048, I=1024, E=32, k=4),
     "w6a8_stream_items": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=512, H=2048, I=1024, E=32, k=4,
                                     I_shared=1024),
+    # the wide E2M1 kernel (K multiples of 512, at least 1024) with two M-tiles
+    # per expert, the second ragged
+    "w4a8_wide_multi_tile": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=600, H=1024, I=1024, E=4, k=2),
     # MXFP8 activations x E2M1 with H not a multiple of 256: the 32x32 tiled
     # kernel instead of the wide one
     "w4a8_h384": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=200, H=384, I=256, E=4, k=2),
