@@ -8,15 +8,21 @@
 // Work item = (16-row M-tile of one expert, N-block of 128 weight rows: FC1
 // 64 gate + 64 up rows, i.e. 64 columns of h; FC2 128 output columns).  The
 // grid is persistent (one workgroup per CU).  Per 256-K stage the weight
-// tile (128 rows x 128 B of E2M1 codes + 8 E8M0 scale bytes per row) and the
-// activation tile (16 rows x 512 B of bf16) are copied global -> LDS into a
-// ring of 6 stage buffers, so up to 5 stages (about 100 KB per CU) are in
-// flight: enough to cover HBM latency at full bandwidth.  Reading 128
-// contiguous bytes of every weight row per stage streams HBM markedly faster
-// than 64 (measured: the decode FC1 went from 4.7 to 5.5 TB/s).
+// tile (128 rows x 128 B of E2M1 codes) and the activation tile (16 rows x
+// 512 B of bf16) are copied global -> LDS into a ring of 6 stage buffers, so
+// up to 5 stages (about 100 KB per CU) are in flight: enough to cover HBM
+// latency at full bandwidth.  Reading 128 contiguous bytes of every weight row
+// per stage streams HBM markedly faster than 64 (measured: the decode FC1 went
+// from 4.7 to 5.5 TB/s).  The E8M0 weight scales (8 bytes per row and stage)
+// travel in groups of GS stages (4, 2 or 1, the largest dividing the stages
+// of an item): a row's scales for consecutive stages are contiguous, and one
+// copy per row and group costs a quarter of the memory requests of one per
+// row and stage (measured: without any scale copies the decode FC1 ran 14%
+// faster).
 //
-// Waves (7): 0-3 multiply, 4-5 copy weights (10 copies per stage each), 6
-// copies activations (8 copies per stage).  Each copy wave owns one in-order stream
+// Waves (7): 0-3 multiply, 4-5 copy weights (8 copies per stage each, plus
+// the scale copies at the start of a group), 6 copies activations (8 copies
+// per stage).  Each copy wave owns one in-order stream
 // and waits for its own stage before the per-stage barrier; the multiply
 // waves issue no loads (item geometry and row metadata come through the
 // scalar cache).
@@ -53,16 +59,28 @@ constexpr int kWaveB = 4;         // weight-copy waves 4, 5
 constexpr int kWaveA = 6;         // activation-copy wave
 constexpr int kThreadsS = 64 * 7;
 
-// stage layout: [weights 128 rows x BROW][scale bytes 128 rows x SBK/32]
-//               [activations 16 rows x 2*SBK]
+// stage layout: [weights 128 rows x BROW][activations 16 rows x 2*SBK];
+// then the scale-group ring: NG(GS) buffers of 128 rows x GS*SBK/32 bytes
 constexpr int S_B = SBN * BROW;
-constexpr int S_BS = SBN * SBK / 32;
 constexpr int S_A = SBM * SBK * 2;
-constexpr int S_STAGE = S_B + S_BS + S_A;
+constexpr int S_STAGE = S_B + S_A;
 constexpr int kBData = S_B / 1024 / 2;        // 1-KB weight copies per weight-copy wave
-constexpr int kBScale = S_BS / 256 / 2;       // 256-B scale copies per weight-copy wave
-constexpr int kBCopies = kBData + kBScale;
 constexpr int kACopiesS = S_A / 1024;
+constexpr int SROW = SBK / 32;                // scale bytes per row and stage
+constexpr int L_SG = NSTAGE * S_STAGE;        // scale-group ring
+constexpr int L_SG_SIZE = 4 * SBN * SROW * 3; // room for the largest ring (GS = 4, 3 buffers)
+// Scale groups of GS stages: group G (stages GS*G ..) is copied just before
+// the code copies of its first stage, into buffer G % NG, whose previous
+// group was last read at stage GS*(G-NG) + GS - 1; stage GS*G is copied
+// after barrier GS*G - NSTAGE + 1, so GS*(NG-1) >= NSTAGE - 1 keeps them apart.
+template <int GS> struct SGroup {
+  static constexpr int NG = (NSTAGE - 1 + GS - 1) / GS + 1;
+  static constexpr int BYTES = SBN * SROW * GS;           // one group buffer
+  static constexpr int LW = SROW * GS >= 16 ? 16 : 4;     // bytes per lane and copy
+  static constexpr int COPIES = BYTES / 2 / (64 * LW);    // per weight-copy wave
+  static_assert(NG * BYTES <= L_SG_SIZE, "scale-group ring");
+  static_assert(GS * (NG - 1) >= NSTAGE - 1, "scale-group ring too short");
+};
 
 // weight tile: 16-B chunk c of row r at slot c ^ swz(r), so that 8 rows read
 // at the same chunk fall in 8 different 16-B bank groups
@@ -116,10 +134,24 @@ __device__ __forceinline__ void wait_stages(int n) {
   }
 }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n in [LO, HI] (binary search
+// over the immediate forms; n above HI waits for HI, which is stricter)
+template <int LO, int HI>
+__device__ __forceinline__ void wait_ops(int n) {
+  if constexpr (LO == HI) {
+    wait_vm_lgkm0<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_ops<MID, HI>(n);
+    else wait_ops<LO, MID - 1>(n);
+  }
+}
+
 // ------------------------------------------------------------ multiply ---
 
-template <bool FC1>
+template <bool FC1, int GS>
 __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc, uint8_t* smem) {
+  using SG = SGroup<GS>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   // B-tile rows of this wave's two 16-column tiles
@@ -132,8 +164,9 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
     wait_lgkm0();
     barrier();
     const uint8_t* st = smem + (gidx % NSTAGE) * S_STAGE;
-    const uint8_t* sb = st + S_B;
-    const uint8_t* as = st + S_B + S_BS;
+    // this stage's scale bytes of row jr: sb[jr * SROW * GS + ...]
+    const uint8_t* sb = smem + L_SG + ((gidx / GS) % SG::NG) * SG::BYTES + (gidx % GS) * SROW;
+    const uint8_t* as = st + S_B;
     // activation run of this lane: row r16, k [KPL*g, KPL*(g+1)) = chunks
     // (KPL/8)*g .. +KPL/8
     constexpr int NA = KPL / 8;  // 16-B activation chunks (MFMA steps) per lane
@@ -147,7 +180,7 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
       for (int blk = 0; blk < KPL / 32; ++blk) {
         // one MX block: 16 B of codes, one scale byte
         const uint4 b = *(const uint4*)(st + wb_off(jr, (KPL / 32) * g + blk));
-        const float sc = e8m0_to_f32(sb[jr * (SBK / 32) + (KPL / 32) * g + blk]);
+        const float sc = e8m0_to_f32(sb[jr * SROW * GS + (KPL / 32) * g + blk]);
         const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
         for (int kq = 0; kq < 4; ++kq) {
@@ -217,15 +250,17 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
 
 // -------------------------------------------------------- weight copies ---
 
-template <bool FC1>
+template <bool FC1, int GS>
 __device__ __forceinline__ void small_weights(const FcArgs& p, const SSched& sc, uint8_t* smem) {
-  const int lane = threadIdx.x & 63, bw = (threadIdx.x >> 6) - kWaveB;
+  using SG = SGroup<GS>;
+  const int lane = threadIdx.x & 63, bw = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) - kWaveB);
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
   const int64_t wrow = (int64_t)K / 2;
   constexpr int CPR = BROW / 16;  // 16-B chunks per weight row and stage
+  constexpr int GROW = SROW * GS; // scale bytes per row and group
   const uint8_t* src[kBData];
-  const uint8_t* ssrc[kBScale];
+  const uint8_t* ssrc[SG::COPIES];
   auto setup = [&](int li) {
     const SGeom it = s_geom(p, sc, li);
     const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride;
@@ -237,23 +272,30 @@ __device__ __forceinline__ void small_weights(const FcArgs& p, const SSched& sc,
       const int ch = (lane % CPR) ^ wb_swz(jr);
       src[i] = wb + s_wrow<FC1>(p, it.nb, jr) * wrow + 16 * ch;
     }
-    // scale bytes: SBK/32 per row and stage; one 4-B lane covers 4 / (SBK/32) rows
+    // scale group: GROW bytes per row, SG::LW per lane; copy t covers bytes
+    // [64 LW t, 64 LW (t+1)) of the group buffer (row-major)
 #pragma unroll
-    for (int i = 0; i < kBScale; ++i) {
-      const int t = kBScale * bw + i;       // 256-B scale copy index
-      const int byte = 256 * t + 4 * lane;  // offset in the stage's scale area
-      const int jr = byte / (SBK / 32), within = byte % (SBK / 32);
+    for (int i = 0; i < SG::COPIES; ++i) {
+      const int byte = SG::LW * (64 * (SG::COPIES * bw + i) + lane);
+      const int jr = byte / GROW, within = byte % GROW;
       ssrc[i] = sb + s_wrow<FC1>(p, it.nb, jr) * (K / 32) + within;
     }
   };
   int li = 0, ls = 0, issued = 0;
   auto issue_next = [&]() {
     if (ls == 0) setup(li);
+    // the scale group first: the stage's own wait then covers it
+    if (issued % GS == 0) {
+      const uint32_t gb = lds0 + L_SG + ((issued / GS) % SG::NG) * SG::BYTES;
+#pragma unroll
+      for (int i = 0; i < SG::COPIES; ++i) {
+        if constexpr (SG::LW == 16) lds_copy16(ssrc[i] + ls * SROW, gb + 64 * SG::LW * (SG::COPIES * bw + i));
+        else lds_copy4(ssrc[i] + ls * SROW, gb + 64 * SG::LW * (SG::COPIES * bw + i));
+      }
+    }
     const uint32_t base = lds0 + (issued % NSTAGE) * S_STAGE;
 #pragma unroll
     for (int i = 0; i < kBData; ++i) lds_copy16(src[i] + ls * BROW, base + 1024 * (kBData * bw + i));
-#pragma unroll
-    for (int i = 0; i < kBScale; ++i) lds_copy4(ssrc[i] + ls * (SBK / 32), base + S_B + 256 * (kBScale * bw + i));
     ++issued;
     if (++ls == sc.nk) {
       ls = 0;
@@ -262,7 +304,10 @@ __device__ __forceinline__ void small_weights(const FcArgs& p, const SSched& sc,
   };
   for (int s = 0; s < NSTAGE - 1 && s < sc.total; ++s) issue_next();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
-    wait_stages<kBCopies, NSTAGE - 2>(issued - 1 - gidx);
+    // stage gidx (and its group, copied before it) has landed once at most the
+    // copies of the stages issued after it remain
+    const int after = (issued - 1 - gidx) * kBData + SG::COPIES * ((issued - 1) / GS - gidx / GS);
+    wait_ops<0, (NSTAGE - 2) * (kBData + SG::COPIES)>(after);
     barrier();
     if (issued < sc.total) issue_next();
   }
@@ -307,7 +352,7 @@ __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched&
   int li = 0, ls = 0, issued = 0;
   auto issue_next = [&]() {
     if (ls == 0) setup(li);
-    const uint32_t base = lds0 + (issued % NSTAGE) * S_STAGE + S_B + S_BS;
+    const uint32_t base = lds0 + (issued % NSTAGE) * S_STAGE + S_B;
 #pragma unroll
     for (int i = 0; i < kACopiesS; ++i) lds_copy16(src[i] + ls * (2 * SBK), base + 1024 * i);
     ++issued;
@@ -326,9 +371,9 @@ __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched&
 
 }  // namespace
 
-template <bool FC1>
+template <bool FC1, int GS>
 __global__ __launch_bounds__(kThreadsS, 1) void k_fc_small(FcArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * S_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L_SG + L_SG_SIZE];
   SSched sc;
   sc.nk = p.K / SBK;
   sc.NB = p.nchunks;
@@ -339,17 +384,25 @@ __global__ __launch_bounds__(kThreadsS, 1) void k_fc_small(FcArgs p) {
   sc.my_items = nitems > sc.q ? (nitems - sc.q + sc.Q - 1) / sc.Q : 0;
   sc.total = sc.my_items * sc.nk;
   if (sc.total == 0) return;
-  const int w = threadIdx.x >> 6;
-  if (w < kMulW) small_multiply<FC1>(p, sc, smem);
-  else if (w < kWaveA) small_weights<FC1>(p, sc, smem);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w < kMulW) small_multiply<FC1, GS>(p, sc, smem);
+  else if (w < kWaveA) small_weights<FC1, GS>(p, sc, smem);
   else small_activations<FC1>(p, sc, smem);
+}
+
+template <bool FC1>
+static hipError_t launch_small_t(const FcArgs& p, int grid, hipStream_t st) {
+  // scale groups: the largest of 4, 2, 1 stages that divides the stages of an item
+  const int nk = p.K / SBK;
+  if (nk % 4 == 0) k_fc_small<FC1, 4><<<grid, kThreadsS, 0, st>>>(p);
+  else if (nk % 2 == 0) k_fc_small<FC1, 2><<<grid, kThreadsS, 0, st>>>(p);
+  else k_fc_small<FC1, 1><<<grid, kThreadsS, 0, st>>>(p);
+  return hipGetLastError();
 }
 
 hipError_t launch_fc_small(const FcArgs& p, bool fc1, int grid, hipStream_t st) {
   if (grid < 1) grid = 1;
-  if (fc1) k_fc_small<true><<<grid, kThreadsS, 0, st>>>(p);
-  else k_fc_small<false><<<grid, kThreadsS, 0, st>>>(p);
-  return hipGetLastError();
+  return fc1 ? launch_small_t<true>(p, grid, st) : launch_small_t<false>(p, grid, st);
 }
 
 }  // namespace moe_mx
