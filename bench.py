@@ -42,10 +42,10 @@ BOUND = {
 }
 # FC1 kernel that bench times per workload (the dominant kernel of the layer)
 FC1_KERNEL = {
-    "tiny_w4a16": "k_fc_small<true>",
-    "decode_w4a16": "k_fc_small<true>",
+    "tiny_w4a16": "k_fc_small<true, 1>",
+    "decode_w4a16": "k_fc_small<true, 4>",
     "prefill_w4a8": "k_fc_wide<true>",
-    "skew_w4a16": "k_fc_small<true>",
+    "skew_w4a16": "k_fc_small<true, 4>",
     "w6a8_shared": "k_fc_tiled<true, 2>",
 }
 
