@@ -239,8 +239,13 @@ struct CopyCount {
 template <bool FC1>
 struct ACopier {
   using Count = CopyCount<kAStages, kACodeCopies>;
-  uint32_t src[kACodeCopies];  // byte offsets into the activations (< 4 GiB)
-  int nb;                      // N-block of the code cursor's item
+  uint32_t src[kACodeCopies];  // FC1 routed: byte offsets into the activations (< 4 GiB)
+  int nb, p0, rows;            // the code cursor's item
+  // FC1 gathers token rows through the row table (or, dense, rows p0 + r), and
+  // keeps the per-lane row offsets for the item; FC2's tile row r is always
+  // activation row p0 + r, so its offsets are recomputed at each issue (no
+  // per-item registers)
+  static constexpr bool kGather = FC1;
 
   // activation row (token for FC1, permuted row for FC2) of tile row r of item li
   __device__ __forceinline__ static uint32_t src_row(const FcArgs& p, const uint8_t* smem, const ItemGeom& it,
@@ -264,16 +269,29 @@ struct ACopier {
         copy_table(p, item_geom(p, sc, li + 1), lds0 + L_TBL + ((li + 1) % kTables) * TABLE, wm == 0);
       const ItemGeom it = item_geom(p, sc, li);
       nb = it.nb;
-      const int c = (lane & 7) ^ (lane >> 3);
+      p0 = it.p0;
+      rows = it.rows;
+      if (kGather) {
+        const int c = (lane & 7) ^ (lane >> 3);
 #pragma unroll
-      for (int i = 0; i < kACodeCopies; ++i)
-        src[i] = src_row(p, smem, it, li, 8 * (kACodeCopies * wm + i) + (lane >> 3)) * (uint32_t)p.K + 16 * c;
+        for (int i = 0; i < kACodeCopies; ++i)
+          src[i] = src_row(p, smem, it, li, 8 * (kACodeCopies * wm + i) + (lane >> 3)) * (uint32_t)p.K + 16 * c;
+      }
     }
     const int ks = k_step(sc, nb, ls);
     const uint8_t* a = (const uint8_t*)p.a + ks * TBK;
     const uint32_t base = lds0 + L_A + (s % kAStages) * A_STAGE;
+    if (kGather) {
 #pragma unroll
-    for (int i = 0; i < kACodeCopies; ++i) lds_copy16_s(a, src[i], base + 1024 * (kACodeCopies * wm + i));
+      for (int i = 0; i < kACodeCopies; ++i) lds_copy16_s(a, src[i], base + 1024 * (kACodeCopies * wm + i));
+    } else {
+      const uint32_t c16 = 16 * ((lane & 7) ^ (lane >> 3));
+#pragma unroll
+      for (int i = 0; i < kACodeCopies; ++i) {
+        const int r = min(8 * (kACodeCopies * wm + i) + (lane >> 3), rows - 1);  // rows past the tile repeat its last row
+        lds_copy16_s(a, (uint32_t)(p0 + r) * (uint32_t)p.K + c16, base + 1024 * (kACodeCopies * wm + i));
+      }
+    }
   }
 
   // scale group G (steps 4G .. 4G+3)
