@@ -34,6 +34,11 @@ CASES = {
     # the wide E2M1 kernel (K multiples of 512, at least 1024) with two M-tiles
     # per expert, the second ragged
     "w4a8_wide_multi_tile": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=600, H=1024, I=1024, E=4, k=2),
+    # the wide kernel in dense mode: an E2M1 shared expert next to routed experts
+    "w4a8_wide_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=256, H=1024, I=1024, E=8, k=2,
+                                   I_shared=1024, wfmt="e2m1"),
+    # the wide kernel with one expert per token (token index = assignment id)
+    "w4a8_wide_k1": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=400, H=1024, I=1024, E=4, k=1),
     # MXFP8 activations x E2M1 with H not a multiple of 256: the 32x32 tiled
     # kernel instead of the wide one
     "w4a8_h384": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=200, H=384, I=256, E=4, k=2),
