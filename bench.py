@@ -45,14 +45,14 @@ FC1_KERNEL = {
     "tiny_w4a16": "k_fc_small<true, 1>",
     "decode_w4a16": "k_fc_small<true, 4>",
     "prefill_w4a8": "k_fc_wide<true>",
-    "skew_w4a16": "k_fc_small<true, 4>",
+    "skew_w4a16": "k_fc_mid<true>",
     "w6a8_shared": "k_fc_tiled<true, 2>",
 }
 
 # Sources of the GEMM kernels: a committed HBM-traffic summary counts only
 # while these are unchanged since it was taken.
 KERNEL_SOURCES = tuple(f"block_scaled_precision_amd/csrc/{f}" for f in (
-    "copy_ring.h", "gemm.h", "gemm_small.hip", "gemm_stream.hip", "gemm_tiled.hip", "gemm_wide.hip",
+    "copy_ring.h", "gemm.h", "gemm_mid.hip", "gemm_small.hip", "gemm_stream.hip", "gemm_tiled.hip", "gemm_wide.hip",
     "internal.h", "mx_device.h"))
 
 

@@ -130,11 +130,28 @@ static int wbits(mx_elem_t f) { return f == MX_E2M1 ? 4 : (f == MX_E3M2 ? 6 : 8)
 // activations are MXFP8 and the local experts average at least this many rows;
 // otherwise the stream kernels (16-row tiles, weights straight from HBM) run.
 constexpr int kTiledMinRowsPerExpert = 16;
+// bf16 activations: the mid-M kernel (64-row tiles) when the local experts
+// average at least this many rows, else the small-M kernel (16-row tiles).
+constexpr int kMidMinRowsPerExpert = 32;
+
+// GEMM kernel family of one FC1/FC2 pair
+enum class Fc { kStream, kSmall, kMid, kTiled, kWide };
+
+// N-block width: FC1 in h columns, FC2 in output columns
+static int fc_cols(Fc k, bool fc1) {
+  switch (k) {
+    case Fc::kWide:
+    case Fc::kMid: return fc1 ? kWideCols / 2 : kWideCols;
+    case Fc::kTiled:
+    case Fc::kSmall: return fc1 ? kTiledColsFc1 : kTiledColsFc2;
+    default: return fc1 ? kStreamColsFc1 : kStreamColsFc2;
+  }
+}
 
 struct FusedPlan {
   int L, off;
   int64_t A;
-  bool tiled, shared_tiled, wide, shared_wide;
+  Fc routed, shared;
   int bm;
   int nblk, max_tiles;
   size_t ids, w, rank, hist, offsets, sorted, sorted_w, tiles, ntiles, xq, xs, h, hsc, hs, hssc, obuf, sbuf, total;
@@ -146,18 +163,33 @@ static FusedPlan plan(const moe_problem_t& p) {
   f.L = p.local_num_experts == 0 ? p.E : p.local_num_experts;
   f.A = (int64_t)p.T * p.k;
   f.nblk = (p.T + kTokensPerRouteBlock - 1) / kTokensPerRouteBlock;
-  const bool mxa = p.act == MOE_ACT_MXFP8;
-  f.tiled = mxa && f.L > 0 && f.A >= (int64_t)kTiledMinRowsPerExpert * f.L && p.H >= kTiledMinK &&
-            p.I >= kTiledMinK;
-  f.shared_tiled = mxa && p.T >= kTiledMinRowsPerExpert && p.H >= kTiledMinK && p.I_shared >= kTiledMinK;
-  // E2M1 weights take the wide tiled kernel (256-row weight blocks)
-  // (K a multiple of 512 and at least 1024: scale groups of 4 K-steps, items of
-  // at least 8 steps; A*k < 2^32: tokens from assignment ids by multiplication)
-  const bool wide_k = p.H % 512 == 0 && p.I % 512 == 0 && p.H >= 1024 && p.I >= 1024;
-  f.wide = f.tiled && p.w_fmt == MX_E2M1 && wide_k && (double)f.A * p.k < 4294967296.0;
-  f.shared_wide = f.shared_tiled && p.w_fmt == MX_E2M1 && p.H % 512 == 0 && p.H >= 1024 &&
-                  p.I_shared % 512 == 0 && p.I_shared >= 1024;
-  f.bm = f.tiled ? kTiledRows : kStreamRows;
+  // tokens from assignment ids by multiplication (FC1 gathers of the wide and
+  // mid kernels) need A*k < 2^32
+  const bool kdiv_ok = (double)f.A * p.k < 4294967296.0;
+  if (p.act == MOE_ACT_MXFP8) {
+    const bool tiled = f.L > 0 && f.A >= (int64_t)kTiledMinRowsPerExpert * f.L && p.H >= kTiledMinK &&
+                       p.I >= kTiledMinK;
+    const bool shared_tiled = p.T >= kTiledMinRowsPerExpert && p.H >= kTiledMinK && p.I_shared >= kTiledMinK;
+    // E2M1 weights take the wide tiled kernel (256-row weight blocks)
+    // (K a multiple of 512 and at least 1024: scale groups of 4 K-steps, items
+    // of at least 8 steps)
+    const bool wide_h = p.w_fmt == MX_E2M1 && p.H % 512 == 0 && p.H >= 1024;
+    const bool wide = tiled && wide_h && p.I % 512 == 0 && p.I >= 1024 && kdiv_ok;
+    const bool shared_wide = shared_tiled && wide_h && p.I_shared % 512 == 0 && p.I_shared >= 1024;
+    f.routed = wide ? Fc::kWide : (tiled ? Fc::kTiled : Fc::kStream);
+    f.shared = shared_wide ? Fc::kWide : (shared_tiled ? Fc::kTiled : Fc::kStream);
+  } else {
+    // bf16 activations (E2M1 weights): the small-M kernel, or the mid-M kernel
+    // for experts with many rows; the stream kernels when K does not fit them
+    const bool small = p.H % kSmallK == 0 && p.I % kSmallK == 0 && p.I_shared % kSmallK == 0;
+    const bool mid_h = small && p.H % kMidK == 0;
+    const bool mid = mid_h && p.I % kMidK == 0 && f.L > 0 && f.A >= (int64_t)kMidMinRowsPerExpert * f.L && kdiv_ok;
+    const bool shared_mid = mid_h && p.I_shared % kMidK == 0 && p.T >= kMidMinRowsPerExpert;
+    f.routed = mid ? Fc::kMid : (small ? Fc::kSmall : Fc::kStream);
+    f.shared = shared_mid ? Fc::kMid : (small ? Fc::kSmall : Fc::kStream);
+  }
+  f.bm = (f.routed == Fc::kTiled || f.routed == Fc::kWide) ? kTiledRows
+                                                           : (f.routed == Fc::kMid ? kMidRows : kStreamRows);
   f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -375,26 +407,20 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.ws_estride = 2 * (int64_t)I * (H / 32);
   a1.K = H;
   a1.N = I;
-  // bf16 activations (E2M1 weights): the small-M kernel; MXFP8 activations:
-  // the tiled kernel when rows per expert allow, else the stream kernel
-  const bool small = !mx && H % kSmallK == 0 && I % kSmallK == 0 && Is % kSmallK == 0;
-  // N-block width of each variant: FC1 in h columns, FC2 in output columns
-  auto cols_fc1 = [&](bool tiled, bool wide) {
-    return wide ? kWideCols / 2 : ((tiled || small) ? kTiledColsFc1 : kStreamColsFc1);
-  };
-  auto cols_fc2 = [&](bool tiled, bool wide) {
-    return wide ? kWideCols : ((tiled || small) ? kTiledColsFc2 : kStreamColsFc2);
-  };
-  a1.nchunks = I / cols_fc1(f.tiled, f.wide);
+  a1.nchunks = I / fc_cols(f.routed, true);
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
   const int cus = device_cus();
-  auto launch_fc = [&](const FcArgs& a, bool fc1, bool tiled, bool wide) {
-    if (small) return launch_fc_small(a, fc1, cus, stream);
-    if (wide) return launch_fc_wide(a, fc1, cus, stream);
-    return tiled ? launch_fc_tiled(a, fc1, wf, cus, stream) : launch_fc_stream(a, fc1, mx, wf, stream);
+  auto launch_fc = [&](const FcArgs& a, bool fc1, Fc kind) {
+    switch (kind) {
+      case Fc::kSmall: return launch_fc_small(a, fc1, cus, stream);
+      case Fc::kMid: return launch_fc_mid(a, fc1, cus, stream);
+      case Fc::kWide: return launch_fc_wide(a, fc1, cus, stream);
+      case Fc::kTiled: return launch_fc_tiled(a, fc1, wf, cus, stream);
+      default: return launch_fc_stream(a, fc1, mx, wf, stream);
+    }
   };
-  if (!ok(launch_fc(a1, true, f.tiled, f.wide))) return MOE_ERR_HIP;
+  if (!ok(launch_fc(a1, true, f.routed))) return MOE_ERR_HIP;
   // 6-7. FC2 + weighted combine into the fp32 accumulator
   if (!mark(MOE_STAGE_FC2)) return MOE_ERR_HIP;
   FcArgs a2 = a1;
@@ -406,10 +432,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a2.ws_estride = (int64_t)H * (I / 32);
   a2.K = I;
   a2.N = H;
-  a2.nchunks = H / cols_fc2(f.tiled, f.wide);
+  a2.nchunks = H / fc_cols(f.routed, false);
   a2.out = nullptr;
   a2.obuf = obuf;
-  if (!ok(launch_fc(a2, false, f.tiled, f.wide))) return MOE_ERR_HIP;
+  if (!ok(launch_fc(a2, false, f.routed))) return MOE_ERR_HIP;
   // shared expert: a dense expert over all T tokens with its own weight
   if (!mark(MOE_STAGE_SHARED)) return MOE_ERR_HIP;
   if (Is > 0) {
@@ -421,10 +447,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s1.w_estride = 0;
     s1.ws_estride = 0;
     s1.N = Is;
-    s1.nchunks = Is / cols_fc1(f.shared_tiled, f.shared_wide);
+    s1.nchunks = Is / fc_cols(f.shared, true);
     s1.out = ws + f.hs;
     s1.out_scale = (uint8_t*)(ws + f.hssc);
-    if (!ok(launch_fc(s1, true, f.shared_tiled, f.shared_wide))) return MOE_ERR_HIP;
+    if (!ok(launch_fc(s1, true, f.shared))) return MOE_ERR_HIP;
     FcArgs s2 = a2;
     s2.dense_rows = T;
     s2.dense_weight = p->shared_weight;
@@ -435,10 +461,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s2.w_estride = 0;
     s2.ws_estride = 0;
     s2.K = Is;
-    s2.nchunks = H / cols_fc2(f.shared_tiled, f.shared_wide);
+    s2.nchunks = H / fc_cols(f.shared, false);
     s2.obuf = sbuf;
     (void)bytes_is;
-    if (!ok(launch_fc(s2, false, f.shared_tiled, f.shared_wide))) return MOE_ERR_HIP;
+    if (!ok(launch_fc(s2, false, f.shared))) return MOE_ERR_HIP;
   }
   // 8. y = bf16(accumulator)
   if (!mark(MOE_STAGE_FINALIZE)) return MOE_ERR_HIP;

@@ -42,6 +42,17 @@ CASES = {
     # MXFP8 activations x E2M1 with H not a multiple of 256: the 32x32 tiled
     # kernel instead of the wide one
     "w4a8_h384": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=200, H=384, I=256, E=4, k=2),
+    # bf16 activations, experts averaging at least 32 rows: the 64-row mid-M
+    # kernel; skewed routing gives experts of several M-tiles, ragged tails and
+    # two experts with no rows
+    "skew_w4a16_mid": gen.scaled(gen.WORKLOADS["skew_w4a16"], T=512, H=1024, I=512, E=16, k=4),
+    # the mid-M kernel over many items per workgroup
+    "w4a16_mid_items": gen.scaled(gen.WORKLOADS["skew_w4a16"], T=1024, H=2048, I=1024, E=8, k=4),
+    # the mid-M kernel in dense mode (bf16 shared expert, last M-tile of 8 rows)
+    "w4a16_mid_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=200, H=512, I=512, E=4, k=2,
+                                   I_shared=1024, wfmt="e2m1", act="bf16"),
+    # the mid-M kernel with one expert per token (token index = assignment id)
+    "w4a16_mid_k1": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=300, H=512, I=1024, E=4, k=1),
     # bf16 activations with I not a multiple of 256: the 16-row stream kernels
     "w4a16_k384": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=40, H=384, I=384, E=8, k=2),
 }
