@@ -49,15 +49,17 @@ constexpr int kStreamRows = 16;
 
 hipError_t launch_fc_stream(const FcArgs& p, bool fc1, bool mx_act, int wfmt, hipStream_t st);
 
-// Tiled variant (MXFP8 activations): M-tiles of up to kTiledRows rows, N-blocks
-// of 64 h columns (FC1: nchunks = I / 64) or 128 output columns (FC2:
-// nchunks = H / 128); `grid` persistent workgroups (rounded down to a multiple
-// of 8, at least 8).  Requires K >= kTiledMinK.
+// Tiled variant (MXFP8 activations): M-tiles of up to `rows` rows (kTiledRows,
+// or kTiledRowsLow when experts see fewer rows: less LDS for activations, a
+// deeper weight ring), N-blocks of 64 h columns (FC1: nchunks = I / 64) or 128
+// output columns (FC2: nchunks = H / 128); `grid` persistent workgroups (rounded
+// down to a multiple of 8, at least 8).  Requires K >= kTiledMinK.
 constexpr int kTiledRows = 192;
+constexpr int kTiledRowsLow = 128;
 constexpr int kTiledColsFc1 = 64;
 constexpr int kTiledColsFc2 = 128;
 constexpr int kTiledMinK = 256;
-hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int grid, hipStream_t st);
+hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int rows, int grid, hipStream_t st);
 
 // Wide variant (MXFP8 activations x E2M1 weights): M-tiles of up to kTiledRows
 // rows, N-blocks of kWideCols weight rows, i.e. 128 h columns (FC1: nchunks =

@@ -7,7 +7,8 @@
 //
 // Work item = (M-tile, N-block).  An M-tile holds up to 192 permuted rows of one
 // expert, so an expert with <= 192 assignments streams its weights from HBM
-// exactly once; the N-block is 128 weight rows (FC1: 64 gate rows and the 64
+// exactly once (128 rows when the experts average at most 96: the activation
+// ring shrinks and the weight ring deepens); the N-block is 128 weight rows (FC1: 64 gate rows and the 64
 // matching up rows, i.e. 64 columns of h; FC2: 128 output columns).  The grid is
 // persistent: one workgroup per CU walks the items of its XCD (whole M-tiles
 // x, x+8, ..., then an equal share of the N-blocks of the last ntiles % 8
@@ -25,9 +26,9 @@
 //    row and stage, plus the per-row scale words) into a ring of 4 LDS
 //    buffers, three stages ahead of the multiply;
 //  * waves 10-11 copy the weight stage (64 B per row and stage for E2M1, 96 B
-//    for E3M2, plus scale words) into a deeper ring (6 buffers for E2M1, 4 for
-//    E3M2) so that weights, which come from HBM, are requested 5 (3) stages
-//    ahead.
+//    for E3M2, plus scale words) into a deeper ring (with 192-row tiles 6
+//    buffers for E2M1, 4 for E3M2; with 128-row tiles 10 and 7) so that
+//    weights, which come from HBM, are requested further ahead.
 // The copies are global_load_lds (global memory straight into LDS) issued from
 // inline assembly; each copy wave waits for its own stage with an explicit
 // vmcnt before the barrier.  Because a wave's memory counter drains in order,
@@ -56,7 +57,6 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int TBM = kTiledRows;  // rows per M-tile (6 sub-blocks of 32)
 constexpr int TBN = 128;         // weight rows per work item
 constexpr int TBK = 128;         // K per stage
 #ifndef MOE_TILED_MUL_WAVES
@@ -68,37 +68,49 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveA = kComputeWaves;      // first activation-copy wave
 constexpr int kWaveB = kComputeWaves + 2;  // first weight-copy wave
 constexpr int kGroupsM = kComputeWaves / 2;  // multiply waves along M
-constexpr int kMaxSub = (kTiledRows / 32 + kGroupsM - 1) / kGroupsM;  // 32-row sub-blocks per multiply wave
 
-// LDS layout: [A ring: 4 x (codes TBM x 128 B + scale words TBM x 4 B)]
+// LDS layout: [A ring: STAGES x (codes TM x 128 B + scale words TM x 4 B)]
 //             [B ring: NBS x (weights + scale words 512 B)]
-//             [row tables: 4 x (source row TBM x 4 B + weight TBM x 4 B)]
-constexpr int kAStages = 4;
-constexpr int kTables = 4;
-static_assert(TBM % 64 == 0 && TBM <= 256, "tile rows");
-constexpr int kACodeCopies = TBM / 16;  // 1-KB code copies per activation-copy wave
-constexpr int kAScaleCopies = TBM / 64; // 256-B scale copies in a stage (both waves)
-constexpr int A_CODES = TBM * TBK;
-constexpr int A_STAGE = A_CODES + TBM * 4;
-template <int WF> struct BLay {
+//             [row tables: TABLES x (source row TM x 4 B + weight TM x 4 B)]
+// for M-tiles of TM rows (kTiledRows or kTiledRowsLow).
+template <int TM> struct ALay {
+  static_assert(TM % 64 == 0 && TM <= 256, "tile rows");
+  static constexpr int STAGES = 4;
+  // The row table of item i+1 is copied with item i's first stage, STAGES - 1
+  // steps before item i starts, into the buffer of item i+1-TABLES, whose last
+  // reader is its epilogue at the end of item i+2-TABLES: with items of at
+  // least 2 steps the copy comes after that epilogue.
+  static constexpr int TABLES = 4;
+  static_assert((TABLES - 2) * 2 >= STAGES, "row table ring too short");
+  static constexpr int MAX_SUB = (TM / 32 + kGroupsM - 1) / kGroupsM;  // 32-row sub-blocks per multiply wave
+  static constexpr int CODE_COPIES = TM / 16;  // 1-KB code copies per activation-copy wave
+  static constexpr int SCALE_COPIES = TM / 64; // 256-B scale copies in a stage (both waves)
+  static constexpr int CODES = TM * TBK;
+  static constexpr int STAGE = CODES + TM * 4;
+  static constexpr int TABLE = TM * 8;
+  static constexpr int COPIES = CODE_COPIES + 2;  // per copy wave and stage: codes + two scale copies
+};
+// The weight ring takes what the activation ring and the tables leave of the
+// LDS: with shorter M-tiles more weight stages (which come from HBM) are in
+// flight.
+template <int WF, int TM> struct BLay {
   static constexpr int ROW = WF == 1 ? 64 : 96;    // bytes of one weight row per stage
   static constexpr int CODES = TBN * ROW;
   static constexpr int STAGE = CODES + TBN * 4;
   static constexpr int COPIES = CODES / 1024;      // 1-KB copies per stage: 8 or 12
   static constexpr int PER_WAVE = COPIES / 2;      // per weight-copy wave: 4 or 6
-  static constexpr int NBS = WF == 1 ? 6 : 4;      // ring depth
+  static constexpr int NBS = TM == kTiledRows ? (WF == 1 ? 6 : 4) : (WF == 1 ? 10 : 7);  // ring depth
+  static_assert((NBS - 2) * (PER_WAVE + 1) < 64, "vmcnt range");
 };
-constexpr int TABLE = TBM * 8;
-template <int WF> struct Lds {
+template <int WF, int TM> struct Lds {
   static constexpr int A = 0;
-  static constexpr int B = kAStages * A_STAGE;
-  static constexpr int TBL = B + BLay<WF>::NBS * BLay<WF>::STAGE;
-  static constexpr int TOTAL = TBL + kTables * TABLE;
+  static constexpr int B = ALay<TM>::STAGES * ALay<TM>::STAGE;
+  static constexpr int TBL = B + BLay<WF, TM>::NBS * BLay<WF, TM>::STAGE;
+  static constexpr int TOTAL = TBL + ALay<TM>::TABLES * ALay<TM>::TABLE;
+  static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
-// copies per copy-wave and stage: codes + two scale-word copies
-constexpr int kACopies = kACodeCopies + 2;
-template <int WF> constexpr int b_copies() { return BLay<WF>::PER_WAVE + 1; }
+template <int WF, int TM> constexpr int b_copies() { return BLay<WF, TM>::PER_WAVE + 1; }
 
 // A tile: row r holds 8 chunks of 16 B; chunk c sits at slot c ^ (r & 7) so
 // that 8 consecutive rows read at the same k land in 8 different bank groups.
@@ -133,6 +145,7 @@ struct Sched {
   int xcd, full, tail0, q, Q, NB, nk, my_items, total;
 };
 
+template <int TM>
 __device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, const Sched& sc, int li) {
   const int j = sc.q + li * sc.Q;
   int ti;
@@ -147,8 +160,8 @@ __device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, const Sched& sc, 
   }
   if (p.dense_rows > 0) {
     g.expert = 0;
-    g.p0 = TBM * ti;
-    g.rows = min(TBM, p.dense_rows - TBM * ti);
+    g.p0 = TM * ti;
+    g.rows = min(TM, p.dense_rows - TM * ti);
   } else {
     const Tile t = load_tile(p.tiles, ti);
     g.expert = t.expert;
@@ -179,12 +192,12 @@ __device__ __forceinline__ int64_t w_row(const FcArgs& p, int nb, int jr) {
 
 // One 128-K stage for a wave holding NM (1 to kMaxSub) sub-blocks: sub-block
 // wm + kGroupsM*m of the tile times the wave's two 32-column B tiles.
-template <int WF, int NM>
-__device__ __forceinline__ void compute_stage(v16f (&acc)[kMaxSub][2], const uint8_t* as, const uint8_t* bs, int wm,
-                                              int brow0, int brow1) {
-  using BL = BLay<WF>;
+template <int WF, int TM, int NM>
+__device__ __forceinline__ void compute_stage(v16f (&acc)[ALay<TM>::MAX_SUB][2], const uint8_t* as, const uint8_t* bs,
+                                              int wm, int brow0, int brow1) {
+  using BL = BLay<WF, TM>;
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
-  const uint32_t* SAs = (const uint32_t*)(as + A_CODES);
+  const uint32_t* SAs = (const uint32_t*)(as + ALay<TM>::CODES);
   const uint32_t* SBs = (const uint32_t*)(bs + BL::CODES);
   v8i bv[2][2];
   uint32_t bsw[2];
@@ -243,10 +256,12 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[kMaxSub][2], const uin
   }
 }
 
-template <bool FC1, int WF>
+template <bool FC1, int WF, int TM>
 __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
-  using L = Lds<WF>;
-  using BL = BLay<WF>;
+  using L = Lds<WF, TM>;
+  using BL = BLay<WF, TM>;
+  using AL = ALay<TM>;
+  constexpr int kMaxSub = AL::MAX_SUB;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   // 8 waves: (wm, wn) = (w / 2, w % 2), so the two multiply waves of a SIMD
   // (w and w + 4) hold sub-blocks {wm, wm + 4} and {wm + 2, wm + 6};
@@ -268,25 +283,25 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
   // sub-blocks of this wave in a tile of `rows` rows
   auto wave_subs = [&](int rows) { return max(0, (((rows + 31) >> 5) - wm + kGroupsM - 1) / kGroupsM); };
   int ci = 0, cs = 0;
-  ItemGeom it = item_geom(p, sc, 0);
+  ItemGeom it = item_geom<TM>(p, sc, 0);
   int nm = wave_subs(it.rows);
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     wait_lgkm0();  // this wave's reads of the previous stage are done
     barrier();
-    const uint8_t* as = smem + L::A + (gidx % kAStages) * A_STAGE;
+    const uint8_t* as = smem + L::A + (gidx % AL::STAGES) * AL::STAGE;
     const uint8_t* bs = smem + L::B + (gidx % BL::NBS) * BL::STAGE;
     switch (nm) {
-      case 4: if constexpr (kMaxSub >= 4) compute_stage<WF, 4>(acc, as, bs, wm, brow0, brow1); break;
-      case 3: if constexpr (kMaxSub >= 3) compute_stage<WF, 3>(acc, as, bs, wm, brow0, brow1); break;
-      case 2: compute_stage<WF, 2>(acc, as, bs, wm, brow0, brow1); break;
-      case 1: compute_stage<WF, 1>(acc, as, bs, wm, brow0, brow1); break;
+      case 4: if constexpr (kMaxSub >= 4) compute_stage<WF, TM, 4>(acc, as, bs, wm, brow0, brow1); break;
+      case 3: if constexpr (kMaxSub >= 3) compute_stage<WF, TM, 3>(acc, as, bs, wm, brow0, brow1); break;
+      case 2: if constexpr (kMaxSub >= 2) compute_stage<WF, TM, 2>(acc, as, bs, wm, brow0, brow1); break;
+      case 1: compute_stage<WF, TM, 1>(acc, as, bs, wm, brow0, brow1); break;
       default: break;
     }
     if (++cs < sc.nk) continue;
 
     // ---- epilogue of item ci ----
-    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (ci % kTables) * TABLE);
-    const float* twt = (const float*)(smem + L::TBL + (ci % kTables) * TABLE + TBM * 4);
+    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (ci % AL::TABLES) * AL::TABLE);
+    const float* twt = (const float*)(smem + L::TBL + (ci % AL::TABLES) * AL::TABLE + TM * 4);
 #pragma unroll
     for (int m = 0; m < kMaxSub; ++m) {
       if (m >= nm) continue;
@@ -334,7 +349,7 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
         for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.f;
     cs = 0;
     if (++ci < sc.my_items) {
-      it = item_geom(p, sc, ci);
+      it = item_geom<TM>(p, sc, ci);
       nm = wave_subs(it.rows);
     }
   }
@@ -348,20 +363,25 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
 // row.  Both activation waves copy the ids (the same bytes to the same place),
 // so each reads only what its own copies wrote; the first also copies the
 // weights, which only the multiply waves read, barriers later.
+template <int TM>
 __device__ __forceinline__ void copy_table(const FcArgs& p, const ItemGeom& it, uint32_t tbl) {
   const int lane = threadIdx.x & 63, aw = (threadIdx.x >> 6) - kWaveA;
 #pragma unroll
-  for (int t = 0; t < TBM / 64; ++t) {
+  for (int t = 0; t < TM / 64; ++t) {
     const int r = 64 * t + lane;
     const int prow = it.p0 + (r < it.rows ? r : 0);
     lds_copy4(p.sorted_assign + prow, tbl + 256 * t);
-    if (aw == 0) lds_copy4(p.sorted_w + prow, tbl + TBM * 4 + 256 * t);
+    if (aw == 0) lds_copy4(p.sorted_w + prow, tbl + TM * 4 + 256 * t);
   }
 }
 
-template <bool FC1, int WF>
+template <bool FC1, int WF, int TM>
 __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
-  using L = Lds<WF>;
+  using L = Lds<WF, TM>;
+  using AL = ALay<TM>;
+  constexpr int kACodeCopies = AL::CODE_COPIES;
+  constexpr int kAScaleCopies = AL::SCALE_COPIES;
+  constexpr int kACopies = AL::COPIES;
   const int lane = threadIdx.x & 63, aw = (threadIdx.x >> 6) - kWaveA;
   const int K = p.K;
   const bool routed = p.dense_rows == 0;
@@ -373,9 +393,9 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
   int load_nb = 0;
   // source rows of item li; its row table must have landed
   auto setup = [&](int li) {
-    const ItemGeom it = item_geom(p, sc, li);
+    const ItemGeom it = item_geom<TM>(p, sc, li);
     load_nb = it.nb;
-    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (li % kTables) * TABLE);
+    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (li % AL::TABLES) * AL::TABLE);
     auto src_row = [&](int r) -> int64_t {
       r = r < it.rows ? r : it.rows - 1;  // rows past the tile repeat its last row
       if (!routed) return it.p0 + r;
@@ -392,18 +412,18 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
     for (int i = 0; i < 2; ++i) ssrc[i] = p.a_scale + src_row(64 * min(2 * aw + i, kAScaleCopies - 1) + lane) * (K / 32);
   };
   auto issue = [&](int s, int buf) {
-    const uint32_t base = lds0 + L::A + buf * A_STAGE;
+    const uint32_t base = lds0 + L::A + buf * AL::STAGE;
 #pragma unroll
     for (int i = 0; i < kACodeCopies; ++i) lds_copy16(asrc[i] + s * TBK, base + 1024 * (kACodeCopies * aw + i));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      lds_copy4(ssrc[i] + 4 * s, base + A_CODES + 256 * min(2 * aw + i, kAScaleCopies - 1));
+      lds_copy4(ssrc[i] + 4 * s, base + AL::CODES + 256 * min(2 * aw + i, kAScaleCopies - 1));
   };
 
   // load cursor: item li, stage ls; stages issued so far
   int li = 0, ls = 0, issued = 0;
   if (routed) {
-    copy_table(p, item_geom(p, sc, 0), lds0 + L::TBL);
+    copy_table<TM>(p, item_geom<TM>(p, sc, 0), lds0 + L::TBL);
     wait_vm_lgkm0<0>();
   }
   // issue the next stage; at the start of an item, first copy the next item's
@@ -412,10 +432,10 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
   auto issue_next = [&]() {
     if (ls == 0) {
       if (routed && li + 1 < sc.my_items)
-        copy_table(p, item_geom(p, sc, li + 1), lds0 + L::TBL + ((li + 1) % kTables) * TABLE);
+        copy_table<TM>(p, item_geom<TM>(p, sc, li + 1), lds0 + L::TBL + ((li + 1) % AL::TABLES) * AL::TABLE);
       setup(li);
     }
-    issue(k_stage(sc, load_nb, ls), issued % kAStages);
+    issue(k_stage(sc, load_nb, ls), issued % AL::STAGES);
     ++issued;
     if (++ls == sc.nk) {
       ls = 0;
@@ -426,10 +446,10 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
       if (li < sc.my_items) wait_vm_lgkm0<kACopies>();
     }
   };
-  for (int s = 0; s < kAStages - 1 && s < sc.total; ++s) issue_next();
+  for (int s = 0; s < AL::STAGES - 1 && s < sc.total; ++s) issue_next();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     // stage gidx has landed once at most the stages issued after it remain
-    wait_stages<kACopies, kAStages - 2>(issued - 1 - gidx);
+    wait_stages<kACopies, AL::STAGES - 2>(issued - 1 - gidx);
     barrier();
     if (issued < sc.total) issue_next();
   }
@@ -439,10 +459,10 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
 
 
 
-template <bool FC1, int WF>
+template <bool FC1, int WF, int TM>
 __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
-  using L = Lds<WF>;
-  using BL = BLay<WF>;
+  using L = Lds<WF, TM>;
+  using BL = BLay<WF, TM>;
   const int lane = threadIdx.x & 63, bw = (threadIdx.x >> 6) - kWaveB;
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
@@ -452,7 +472,7 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
   const uint8_t* ssrc;
   int load_nb = 0;
   auto setup = [&](int li) {
-    const ItemGeom it = item_geom(p, sc, li);
+    const ItemGeom it = item_geom<TM>(p, sc, li);
     load_nb = it.nb;
     const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride;
     const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride;
@@ -490,7 +510,7 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
   for (int s = 0; s < BL::NBS - 1 && s < sc.total; ++s) issue_next();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     // stage gidx has landed once at most the stages issued after it remain
-    wait_stages<b_copies<WF>(), BL::NBS - 2>(issued - 1 - gidx);
+    wait_stages<b_copies<WF, TM>(), BL::NBS - 2>(issued - 1 - gidx);
     barrier();
     if (issued < sc.total) issue_next();
   }
@@ -498,13 +518,13 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
 
 }  // namespace
 
-template <bool FC1, int WF>
+template <bool FC1, int WF, int TM>
 __global__ __launch_bounds__(kThreads, 1) void k_fc_tiled(FcArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<WF>::TOTAL];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<WF, TM>::TOTAL];
   Sched sc;
   sc.nk = p.K / TBK;
   sc.NB = p.nchunks;
-  const int ntiles = p.dense_rows > 0 ? (p.dense_rows + TBM - 1) / TBM : *p.num_tiles;
+  const int ntiles = p.dense_rows > 0 ? (p.dense_rows + TM - 1) / TM : *p.num_tiles;
   sc.xcd = blockIdx.x & 7;
   sc.q = blockIdx.x >> 3;
   sc.Q = gridDim.x >> 3;
@@ -516,22 +536,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_fc_tiled(FcArgs p) {
   sc.total = sc.my_items * sc.nk;  // (item, stage) steps of this workgroup
   if (sc.total == 0) return;
   const int wv = threadIdx.x >> 6;
-  if (wv < kComputeWaves) multiply_role<FC1, WF>(p, sc, smem);
-  else if (wv < kWaveB) activation_role<FC1, WF>(p, sc, smem);
-  else weight_role<FC1, WF>(p, sc, smem);
+  if (wv < kComputeWaves) multiply_role<FC1, WF, TM>(p, sc, smem);
+  else if (wv < kWaveB) activation_role<FC1, WF, TM>(p, sc, smem);
+  else weight_role<FC1, WF, TM>(p, sc, smem);
 }
 
 template <bool FC1, int WF>
-static hipError_t launch_tiled_t(const FcArgs& p, int grid, hipStream_t st) {
-  k_fc_tiled<FC1, WF><<<grid, kThreads, 0, st>>>(p);
+static hipError_t launch_tiled_t(const FcArgs& p, int rows, int grid, hipStream_t st) {
+  if (rows == kTiledRowsLow) k_fc_tiled<FC1, WF, kTiledRowsLow><<<grid, kThreads, 0, st>>>(p);
+  else k_fc_tiled<FC1, WF, kTiledRows><<<grid, kThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 
-hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int grid, hipStream_t st) {
+hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int rows, int grid, hipStream_t st) {
+  if (rows != kTiledRows && rows != kTiledRowsLow) return hipErrorInvalidValue;
   if (grid < 8) grid = 8;
   grid &= ~7;
-  if (fc1) return wfmt == 1 ? launch_tiled_t<true, 1>(p, grid, st) : launch_tiled_t<true, 2>(p, grid, st);
-  return wfmt == 1 ? launch_tiled_t<false, 1>(p, grid, st) : launch_tiled_t<false, 2>(p, grid, st);
+  if (fc1) return wfmt == 1 ? launch_tiled_t<true, 1>(p, rows, grid, st) : launch_tiled_t<true, 2>(p, rows, grid, st);
+  return wfmt == 1 ? launch_tiled_t<false, 1>(p, rows, grid, st) : launch_tiled_t<false, 2>(p, rows, grid, st);
 }
 
 }  // namespace moe_mx

@@ -130,6 +130,9 @@ static int wbits(mx_elem_t f) { return f == MX_E2M1 ? 4 : (f == MX_E3M2 ? 6 : 8)
 // activations are MXFP8 and the local experts average at least this many rows;
 // otherwise the stream kernels (16-row tiles, weights straight from HBM) run.
 constexpr int kTiledMinRowsPerExpert = 16;
+// ... in M-tiles of kTiledRowsLow rows while the local experts average at most
+// this many rows (nearly every expert then fits one such tile)
+constexpr int kTiledLowMaxRowsPerExpert = 96;
 // bf16 activations: the mid-M kernel (64-row tiles) when the local experts
 // average at least this many rows, else the small-M kernel (16-row tiles).
 constexpr int kMidMinRowsPerExpert = 32;
@@ -188,8 +191,10 @@ static FusedPlan plan(const moe_problem_t& p) {
     f.routed = mid ? Fc::kMid : (small ? Fc::kSmall : Fc::kStream);
     f.shared = shared_mid ? Fc::kMid : (small ? Fc::kSmall : Fc::kStream);
   }
-  f.bm = (f.routed == Fc::kTiled || f.routed == Fc::kWide) ? kTiledRows
-                                                           : (f.routed == Fc::kMid ? kMidRows : kStreamRows);
+  if (f.routed == Fc::kWide) f.bm = kTiledRows;
+  else if (f.routed == Fc::kTiled)
+    f.bm = f.A <= (int64_t)kTiledLowMaxRowsPerExpert * f.L ? kTiledRowsLow : kTiledRows;
+  else f.bm = f.routed == Fc::kMid ? kMidRows : kStreamRows;
   f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -411,12 +416,13 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
   const int cus = device_cus();
+  // tiled M-tile height: the routed tile list's, dense (shared expert) kTiledRows
   auto launch_fc = [&](const FcArgs& a, bool fc1, Fc kind) {
     switch (kind) {
       case Fc::kSmall: return launch_fc_small(a, fc1, cus, stream);
       case Fc::kMid: return launch_fc_mid(a, fc1, cus, stream);
       case Fc::kWide: return launch_fc_wide(a, fc1, cus, stream);
-      case Fc::kTiled: return launch_fc_tiled(a, fc1, wf, cus, stream);
+      case Fc::kTiled: return launch_fc_tiled(a, fc1, wf, a.dense_rows > 0 ? kTiledRows : f.bm, cus, stream);
       default: return launch_fc_stream(a, fc1, mx, wf, stream);
     }
   };

@@ -39,6 +39,10 @@ CASES = {
                                    I_shared=1024, wfmt="e2m1"),
     # the wide kernel with one expert per token (token index = assignment id)
     "w4a8_wide_k1": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=400, H=1024, I=1024, E=4, k=1),
+    # the tiled kernel with 128-row M-tiles (experts average at most 96 rows)
+    # under skewed routing: some experts span several tiles, two get none
+    "w6a8_low_rows_skew": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=256, H=512, I=256, E=16, k=4,
+                                     I_shared=0, skew=True),
     # MXFP8 activations x E2M1 with H not a multiple of 256: the 32x32 tiled
     # kernel instead of the wide one
     "w4a8_h384": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=200, H=384, I=256, E=4, k=2),
