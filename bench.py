@@ -280,6 +280,8 @@ def main():
                 "frac": achieved / peak, "traffic": traffic}
     roof["kernel"] = FC1_KERNEL[w.name]
     roof["kernel_ms"] = stage_ms["fc1"]
+    roof["alg_bytes_per_launch"] = work["fc1_bytes"]
+    roof["alg_flops_per_launch"] = work["fc1_flops"]
     roof["kernel_source_sha256_16"] = src_hash
 
     out = {

@@ -77,24 +77,28 @@ struct MGeom {
   int expert, p0, rows, nb;
 };
 
-// Item list of one XCD: first the N-blocks of M-tiles xcd, xcd+8, ... for the
-// 8*full leading tiles (all N-blocks of a tile on one XCD, so its activation
-// rows are shared in one L2), then an equal contiguous share of the N-blocks
-// of the ntiles % 8 remaining tiles.
+// Item list of one XCD: the M-tiles go to the XCDs in groups of G consecutive
+// tiles (group i to XCD i % 8), all N-blocks of a tile on one XCD, so its
+// activation rows are shared in one L2; G is about the number of tiles whose
+// items the XCD's workgroups hold at once, so that consecutive tiles of one
+// expert run together and share its weight N-blocks in L2 too.  The tiles
+// past the last whole round of 8 groups are split as items: each XCD takes an
+// equal contiguous share of their N-blocks.
 struct MSched {
-  int xcd, full, tail0, q, Q, NB, nk, my_items, total;
+  int xcd, G, full, tail0, q, Q, NB, nk, my_items, total;
 };
 
 __device__ __forceinline__ MGeom m_geom(const FcArgs& p, const MSched& sc, int li) {
   const int j = sc.q + li * sc.Q;
   int ti;
   MGeom g;
-  if (j < sc.full * sc.NB) {
-    ti = sc.xcd + 8 * (j / sc.NB);
+  if (j < sc.full * sc.G * sc.NB) {
+    const int idx = j / sc.NB;  // tile of this XCD's list
+    ti = (idx / sc.G) * 8 * sc.G + sc.xcd * sc.G + idx % sc.G;
     g.nb = j % sc.NB;
   } else {
-    const int u = sc.tail0 + j - sc.full * sc.NB;
-    ti = 8 * sc.full + u / sc.NB;
+    const int u = sc.tail0 + j - sc.full * sc.G * sc.NB;
+    ti = 8 * sc.G * sc.full + u / sc.NB;
     g.nb = u % sc.NB;
   }
   if (p.dense_rows > 0) {
@@ -371,10 +375,11 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_fc_mid(FcArgs p) {
   sc.xcd = blockIdx.x & 7;
   sc.q = blockIdx.x >> 3;
   sc.Q = gridDim.x >> 3;
-  sc.full = ntiles / 8;
-  const int tail_items = (ntiles % 8) * sc.NB;
+  sc.G = (sc.Q + sc.NB - 1) / sc.NB;
+  sc.full = ntiles / (8 * sc.G);
+  const int tail_items = (ntiles - 8 * sc.G * sc.full) * sc.NB;
   sc.tail0 = tail_items * sc.xcd / 8;
-  const int nitems = sc.full * sc.NB + tail_items * (sc.xcd + 1) / 8 - sc.tail0;
+  const int nitems = sc.full * sc.G * sc.NB + tail_items * (sc.xcd + 1) / 8 - sc.tail0;
   sc.my_items = nitems > sc.q ? (nitems - sc.q + sc.Q - 1) / sc.Q : 0;
   sc.total = sc.my_items * sc.nk;
   if (sc.total == 0) return;
