@@ -77,12 +77,14 @@ constexpr int kSmallK = 256;
 hipError_t launch_fc_small(const FcArgs& p, bool fc1, int grid, hipStream_t st);
 
 // Mid-M variant for bf16 activations and E2M1 weights when experts see many
-// rows: M-tiles of up to kMidRows rows, N-blocks of kWideCols weight rows, i.e.
-// 128 h columns (FC1: nchunks = I / 128) or 256 output columns (FC2: nchunks =
-// H / 256); `grid` persistent workgroups (rounded down to a multiple of 8, at
-// least 8).  Requires K % kMidK == 0 and, for the FC1 gather, A*k < 2^32.
+// rows: M-tiles of up to `rows` rows (kMidRows or kMidRowsHigh), N-blocks of
+// kWideCols weight rows, i.e. 128 h columns (FC1: nchunks = I / 128) or 256
+// output columns (FC2: nchunks = H / 256); `grid` persistent workgroups
+// (rounded down to a multiple of 8, at least 8).  Requires K % kMidK == 0
+// and, for the FC1 gather, A*k < 2^32.
 constexpr int kMidRows = 64;
+constexpr int kMidRowsHigh = 128;
 constexpr int kMidK = 512;
-hipError_t launch_fc_mid(const FcArgs& p, bool fc1, int grid, hipStream_t st);
+hipError_t launch_fc_mid(const FcArgs& p, bool fc1, int rows, int grid, hipStream_t st);
 
 }  // namespace moe_mx

@@ -40,33 +40,42 @@ namespace moe_mx {
 
 namespace {
 
-constexpr int MBM = kMidRows;   // rows per M-tile
 constexpr int MBN = kWideCols;  // weight rows per item
 constexpr int MBK = 128;        // K per stage
-constexpr int NSTG = 4;         // ring depth
 constexpr int GS = 4;           // stages per scale group
 constexpr int NG = 2;           // scale-group buffers
 constexpr int B_ROW = MBK / 2;  // 64 B of codes per weight row and stage
 constexpr int A_ROW = MBK * 2;  // 256 B of bf16 per activation row and stage
 constexpr int S_B = MBN * B_ROW;
-constexpr int S_A = MBM * A_ROW;
-constexpr int S_STAGE = S_B + S_A;
 constexpr int SROW = MBK / 32;       // scale bytes per row and stage
 constexpr int GROW = SROW * GS;      // scale bytes per row and group
 constexpr int G_BYTES = MBN * GROW;  // one scale-group buffer
-constexpr int L_SG = NSTG * S_STAGE;
-constexpr int L_TOTAL = L_SG + NG * G_BYTES;
-constexpr int kThreadsM = 64 * 8;
 constexpr int kBCopies = S_B / 1024 / 2;      // 1-KB code copies per weight wave and stage
 constexpr int kGCopies = G_BYTES / 1024 / 2;  // 1-KB scale copies per weight wave and group
-constexpr int kACopies = S_A / 1024 / 2;      // 1-KB copies per activation wave and stage
 static_assert(MBK * 4 == kMidK, "the host checks K divisibility against kMidK");
-static_assert(kBCopies * 2048 == S_B && kGCopies * 2048 == G_BYTES && kACopies * 2048 == S_A, "copy split");
-static_assert(L_TOTAL <= 160 * 1024, "LDS");
-// Group G (stages GS*G ..) is copied just before the codes of its first stage,
-// into buffer G % NG, whose previous group was last read at stage
-// GS*(G-NG) + GS - 1; stage GS*G is copied after barrier GS*G - NSTG + 1.
-static_assert(GS * (NG - 1) >= NSTG - 1, "scale-group ring too short");
+static_assert(kBCopies * 2048 == S_B && kGCopies * 2048 == G_BYTES, "copy split");
+
+// Layout for M-tiles of TM rows (kMidRows or kMidRowsHigh): TM / 16 multiply
+// waves (TM / 32 row groups x 2 column halves), then 2 weight-copy and 2
+// activation-copy waves; a ring of NSTG stages [weights | activations] and
+// the scale-group ring.
+template <int TM> struct ML {
+  static constexpr int NSTG = TM == kMidRows ? 4 : 3;
+  static constexpr int S_A = TM * A_ROW;
+  static constexpr int S_STAGE = S_B + S_A;
+  static constexpr int L_SG = NSTG * S_STAGE;
+  static constexpr int L_TOTAL = L_SG + NG * G_BYTES;
+  static constexpr int MUL_WAVES = TM / 16;
+  static constexpr int THREADS = 64 * (MUL_WAVES + 4);
+  static constexpr int A_COPIES = S_A / 1024 / 2;  // 1-KB copies per activation wave and stage
+  static constexpr int A_ROWS = TM / 2;            // tile rows per activation wave
+  static_assert(A_COPIES * 2048 == S_A && 4 * A_COPIES == A_ROWS, "copy split");
+  static_assert(L_TOTAL <= 160 * 1024, "LDS");
+  // Group G (stages GS*G ..) is copied just before the codes of its first
+  // stage, into buffer G % NG, whose previous group was last read at stage
+  // GS*(G-NG) + GS - 1; stage GS*G is copied after barrier GS*G - NSTG + 1.
+  static_assert(GS * (NG - 1) >= NSTG - 1, "scale-group ring too short");
+};
 
 // weight tile: row r holds 4 chunks of 16 B; chunk c sits at slot c ^ ((r >> 1) & 3)
 __device__ __forceinline__ int mb_off(int r, int c) { return r * B_ROW + 16 * (c ^ ((r >> 1) & 3)); }
@@ -88,6 +97,7 @@ struct MSched {
   int xcd, G, full, tail0, q, Q, NB, nk, my_items, total;
 };
 
+template <int TM>
 __device__ __forceinline__ MGeom m_geom(const FcArgs& p, const MSched& sc, int li) {
   const int j = sc.q + li * sc.Q;
   int ti;
@@ -103,8 +113,8 @@ __device__ __forceinline__ MGeom m_geom(const FcArgs& p, const MSched& sc, int l
   }
   if (p.dense_rows > 0) {
     g.expert = 0;
-    g.p0 = MBM * ti;
-    g.rows = min(MBM, p.dense_rows - MBM * ti);
+    g.p0 = TM * ti;
+    g.rows = min(TM, p.dense_rows - TM * ti);
   } else {
     const Tile t = load_tile(p.tiles, ti);
     g.expert = t.expert;
@@ -179,8 +189,9 @@ __device__ __forceinline__ void m_stage(const uint8_t* st, const uint8_t* sg, in
   }
 }
 
-template <bool FC1>
+template <bool FC1, int TM>
 __device__ __forceinline__ void mid_multiply(const FcArgs& p, const MSched& sc, uint8_t* smem, int w) {
+  using L = ML<TM>;
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int wr = w >> 1, wc = w & 1;
@@ -190,14 +201,14 @@ __device__ __forceinline__ void mid_multiply(const FcArgs& p, const MSched& sc, 
 #pragma unroll
     for (int n = 0; n < 8; ++n) acc[m][n] = (v4f){0.f, 0.f, 0.f, 0.f};
   int ci = 0, cs = 0;
-  MGeom it = m_geom(p, sc, 0);
+  MGeom it = m_geom<TM>(p, sc, 0);
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     wait_lgkm0();
     barrier();
     if (it.rows > 32 * wr) {
-      const uint8_t* st = smem + (gidx % NSTG) * S_STAGE;
+      const uint8_t* st = smem + (gidx % L::NSTG) * L::S_STAGE;
       // scale byte of row jr, this stage, MX block g: sg[GROW * jr]
-      const uint8_t* sg = smem + L_SG + ((gidx / GS) % NG) * G_BYTES + (gidx % GS) * SROW + g;
+      const uint8_t* sg = smem + L::L_SG + ((gidx / GS) % NG) * G_BYTES + (gidx % GS) * SROW + g;
       m_stage<FC1>(st, sg, wr, wc, r16, g, acc);
     }
     if (++cs < sc.nk) continue;
@@ -244,14 +255,15 @@ __device__ __forceinline__ void mid_multiply(const FcArgs& p, const MSched& sc, 
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[m][n] = (v4f){0.f, 0.f, 0.f, 0.f};
     cs = 0;
-    if (++ci < sc.my_items) it = m_geom(p, sc, ci);
+    if (++ci < sc.my_items) it = m_geom<TM>(p, sc, ci);
   }
 }
 
 // -------------------------------------------------------- weight copies ---
 
-template <bool FC1>
+template <bool FC1, int TM>
 __device__ __forceinline__ void mid_weights(const FcArgs& p, const MSched& sc, uint8_t* smem, int bw) {
+  using L = ML<TM>;
   const int lane = threadIdx.x & 63;
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
@@ -259,7 +271,7 @@ __device__ __forceinline__ void mid_weights(const FcArgs& p, const MSched& sc, u
   const uint8_t* src[kBCopies];
   const uint8_t* ssrc[kGCopies];
   auto setup = [&](int li) {
-    const MGeom it = m_geom(p, sc, li);
+    const MGeom it = m_geom<TM>(p, sc, li);
     const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride;
     const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride;
 #pragma unroll
@@ -282,11 +294,11 @@ __device__ __forceinline__ void mid_weights(const FcArgs& p, const MSched& sc, u
     if (ls == 0) setup(li);
     // the scale group first: the wait for its first stage then covers it
     if (issued % GS == 0) {
-      const uint32_t gb = lds0 + L_SG + ((issued / GS) % NG) * G_BYTES;
+      const uint32_t gb = lds0 + L::L_SG + ((issued / GS) % NG) * G_BYTES;
 #pragma unroll
       for (int i = 0; i < kGCopies; ++i) lds_copy16(ssrc[i] + ls * SROW, gb + 1024 * (kGCopies * bw + i));
     }
-    const uint32_t base = lds0 + (issued % NSTG) * S_STAGE;
+    const uint32_t base = lds0 + (issued % L::NSTG) * L::S_STAGE;
 #pragma unroll
     for (int i = 0; i < kBCopies; ++i) lds_copy16(src[i] + ls * B_ROW, base + 1024 * (kBCopies * bw + i));
     ++issued;
@@ -295,12 +307,12 @@ __device__ __forceinline__ void mid_weights(const FcArgs& p, const MSched& sc, u
       ++li;
     }
   };
-  for (int s = 0; s < NSTG - 1 && s < sc.total; ++s) issue_next();
+  for (int s = 0; s < L::NSTG - 1 && s < sc.total; ++s) issue_next();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     // stage gidx (and its group, copied before it) has landed once at most the
     // copies of the stages issued after it remain
     const int after = (issued - 1 - gidx) * kBCopies + kGCopies * ((issued - 1) / GS - gidx / GS);
-    wait_n<0, (NSTG - 2) * (kBCopies + kGCopies)>(after);
+    wait_n<0, (L::NSTG - 2) * (kBCopies + kGCopies)>(after);
     barrier();
     if (issued < sc.total) issue_next();
   }
@@ -308,8 +320,10 @@ __device__ __forceinline__ void mid_weights(const FcArgs& p, const MSched& sc, u
 
 // ---------------------------------------------------- activation copies ---
 
-template <bool FC1>
+template <bool FC1, int TM>
 __device__ __forceinline__ void mid_activations(const FcArgs& p, const MSched& sc, uint8_t* smem, int aw) {
+  using L = ML<TM>;
+  constexpr int kACopies = L::A_COPIES;
   const int lane = threadIdx.x & 63;
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
@@ -317,17 +331,18 @@ __device__ __forceinline__ void mid_activations(const FcArgs& p, const MSched& s
   const uint8_t* a = (const uint8_t*)p.a;
   const uint8_t* src[kACopies];
   auto setup = [&](int li) {
-    const MGeom it = m_geom(p, sc, li);
-    // this wave's 32 tile rows: tokens (FC1 routed) from the scalar cache
-    Dw16 ids[2];
+    const MGeom it = m_geom<TM>(p, sc, li);
+    // this wave's A_ROWS tile rows: tokens (FC1 routed) from the scalar cache
+    Dw16 ids[L::A_ROWS / 16];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (gather && it.rows > 32 * aw + 16 * h) ids[h] = load_dw16(p.sorted_assign + it.p0 + 32 * aw + 16 * h);
+    for (int h = 0; h < L::A_ROWS / 16; ++h)
+      if (gather && it.rows > L::A_ROWS * aw + 16 * h)
+        ids[h] = load_dw16(p.sorted_assign + it.p0 + L::A_ROWS * aw + 16 * h);
 #pragma unroll
     for (int i = 0; i < kACopies; ++i) {
-      // copy i lands tile rows 32aw + 4i .. +4, sixteen 16-B slots per row
-      const int q = 4 * i + lane / 16;  // row within the wave's 32
-      const int lr = 32 * aw + q;
+      // copy i lands tile rows A_ROWS*aw + 4i .. +4, sixteen 16-B slots per row
+      const int q = 4 * i + lane / 16;  // row within the wave's A_ROWS
+      const int lr = L::A_ROWS * aw + q;
       int64_t row = 0;                  // rows past the tile copy row 0 of the operand
       if (lr < it.rows) {
         if (gather) {
@@ -348,7 +363,7 @@ __device__ __forceinline__ void mid_activations(const FcArgs& p, const MSched& s
   int li = 0, ls = 0, issued = 0;
   auto issue_next = [&]() {
     if (ls == 0) setup(li);
-    const uint32_t base = lds0 + (issued % NSTG) * S_STAGE + S_B;
+    const uint32_t base = lds0 + (issued % L::NSTG) * L::S_STAGE + S_B;
 #pragma unroll
     for (int i = 0; i < kACopies; ++i) lds_copy16(src[i] + ls * A_ROW, base + 1024 * (kACopies * aw + i));
     ++issued;
@@ -357,21 +372,22 @@ __device__ __forceinline__ void mid_activations(const FcArgs& p, const MSched& s
       ++li;
     }
   };
-  for (int s = 0; s < NSTG - 1 && s < sc.total; ++s) issue_next();
+  for (int s = 0; s < L::NSTG - 1 && s < sc.total; ++s) issue_next();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
-    wait_n<0, (NSTG - 2) * kACopies>((issued - 1 - gidx) * kACopies);
+    wait_n<0, (L::NSTG - 2) * kACopies>((issued - 1 - gidx) * kACopies);
     barrier();
     if (issued < sc.total) issue_next();
   }
 }
 
-template <bool FC1>
-__global__ __launch_bounds__(kThreadsM, 1) void k_fc_mid(FcArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[L_TOTAL];
+template <bool FC1, int TM>
+__global__ __launch_bounds__(ML<TM>::THREADS, 1) void k_fc_mid(FcArgs p) {
+  using L = ML<TM>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L::L_TOTAL];
   MSched sc;
   sc.nk = p.K / MBK;
   sc.NB = p.nchunks;
-  const int ntiles = p.dense_rows > 0 ? (p.dense_rows + MBM - 1) / MBM : *p.num_tiles;
+  const int ntiles = p.dense_rows > 0 ? (p.dense_rows + TM - 1) / TM : *p.num_tiles;
   sc.xcd = blockIdx.x & 7;
   sc.q = blockIdx.x >> 3;
   sc.Q = gridDim.x >> 3;
@@ -384,19 +400,25 @@ __global__ __launch_bounds__(kThreadsM, 1) void k_fc_mid(FcArgs p) {
   sc.total = sc.my_items * sc.nk;
   if (sc.total == 0) return;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w < 4) mid_multiply<FC1>(p, sc, smem, w);
-  else if (w < 6) mid_weights<FC1>(p, sc, smem, w - 4);
-  else mid_activations<FC1>(p, sc, smem, w - 6);
+  if (w < L::MUL_WAVES) mid_multiply<FC1, TM>(p, sc, smem, w);
+  else if (w < L::MUL_WAVES + 2) mid_weights<FC1, TM>(p, sc, smem, w - L::MUL_WAVES);
+  else mid_activations<FC1, TM>(p, sc, smem, w - L::MUL_WAVES - 2);
 }
 
 }  // namespace
 
-hipError_t launch_fc_mid(const FcArgs& p, bool fc1, int grid, hipStream_t st) {
+template <int TM>
+static hipError_t launch_mid_t(const FcArgs& p, bool fc1, int grid, hipStream_t st) {
+  if (fc1) k_fc_mid<true, TM><<<grid, ML<TM>::THREADS, 0, st>>>(p);
+  else k_fc_mid<false, TM><<<grid, ML<TM>::THREADS, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fc_mid(const FcArgs& p, bool fc1, int rows, int grid, hipStream_t st) {
+  if (rows != kMidRows && rows != kMidRowsHigh) return hipErrorInvalidValue;
   if (grid < 8) grid = 8;
   grid &= ~7;
-  if (fc1) k_fc_mid<true><<<grid, kThreadsM, 0, st>>>(p);
-  else k_fc_mid<false><<<grid, kThreadsM, 0, st>>>(p);
-  return hipGetLastError();
+  return rows == kMidRows ? launch_mid_t<kMidRows>(p, fc1, grid, st) : launch_mid_t<kMidRowsHigh>(p, fc1, grid, st);
 }
 
 }  // namespace moe_mx

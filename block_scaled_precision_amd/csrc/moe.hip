@@ -133,9 +133,11 @@ constexpr int kTiledMinRowsPerExpert = 16;
 // ... in M-tiles of kTiledRowsLow rows while the local experts average at most
 // this many rows (nearly every expert then fits one such tile)
 constexpr int kTiledLowMaxRowsPerExpert = 96;
-// bf16 activations: the mid-M kernel (64-row tiles) when the local experts
-// average at least this many rows, else the small-M kernel (16-row tiles).
+// bf16 activations: the mid-M kernel when the local experts average at least
+// this many rows (else the small-M kernel, 16-row tiles), with 128-row tiles
+// from the second threshold on (64-row tiles below it)
 constexpr int kMidMinRowsPerExpert = 32;
+constexpr int kMidHighMinRowsPerExpert = 96;
 
 // GEMM kernel family of one FC1/FC2 pair
 enum class Fc { kStream, kSmall, kMid, kTiled, kWide };
@@ -155,7 +157,8 @@ struct FusedPlan {
   int L, off;
   int64_t A;
   Fc routed, shared;
-  int bm;
+  int bm;         // M-tile height of the routed tile list
+  int shared_bm;  // M-tile height of the shared expert (dense mode)
   int nblk, max_tiles;
   size_t ids, w, rank, hist, offsets, sorted, sorted_w, tiles, ntiles, xq, xs, h, hsc, hs, hssc, obuf, sbuf, total;
 };
@@ -194,7 +197,10 @@ static FusedPlan plan(const moe_problem_t& p) {
   if (f.routed == Fc::kWide) f.bm = kTiledRows;
   else if (f.routed == Fc::kTiled)
     f.bm = f.A <= (int64_t)kTiledLowMaxRowsPerExpert * f.L ? kTiledRowsLow : kTiledRows;
-  else f.bm = f.routed == Fc::kMid ? kMidRows : kStreamRows;
+  else if (f.routed == Fc::kMid)
+    f.bm = f.A >= (int64_t)kMidHighMinRowsPerExpert * f.L ? kMidRowsHigh : kMidRows;
+  else f.bm = kStreamRows;
+  f.shared_bm = f.shared == Fc::kMid ? (p.T >= kMidHighMinRowsPerExpert ? kMidRowsHigh : kMidRows) : kTiledRows;
   f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -416,13 +422,14 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
   const int cus = device_cus();
-  // tiled M-tile height: the routed tile list's, dense (shared expert) kTiledRows
+  // M-tile height: the routed tile list's, or the shared expert's in dense mode
   auto launch_fc = [&](const FcArgs& a, bool fc1, Fc kind) {
+    const int rows = a.dense_rows > 0 ? f.shared_bm : f.bm;
     switch (kind) {
       case Fc::kSmall: return launch_fc_small(a, fc1, cus, stream);
-      case Fc::kMid: return launch_fc_mid(a, fc1, cus, stream);
+      case Fc::kMid: return launch_fc_mid(a, fc1, rows, cus, stream);
       case Fc::kWide: return launch_fc_wide(a, fc1, cus, stream);
-      case Fc::kTiled: return launch_fc_tiled(a, fc1, wf, a.dense_rows > 0 ? kTiledRows : f.bm, cus, stream);
+      case Fc::kTiled: return launch_fc_tiled(a, fc1, wf, rows, cus, stream);
       default: return launch_fc_stream(a, fc1, mx, wf, stream);
     }
   };

@@ -55,6 +55,11 @@ CASES = {
     # the mid-M kernel in dense mode (bf16 shared expert, last M-tile of 8 rows)
     "w4a16_mid_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=200, H=512, I=512, E=4, k=2,
                                    I_shared=1024, wfmt="e2m1", act="bf16"),
+    # 64-row mid-M tiles (experts averaging 32 to 96 rows) under skewed routing,
+    # and in dense mode for a shared expert over fewer than 96 tokens
+    "skew_w4a16_mid64": gen.scaled(gen.WORKLOADS["skew_w4a16"], T=256, H=1024, I=512, E=16, k=4),
+    "w4a16_mid64_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=80, H=512, I=512, E=2, k=1,
+                                     I_shared=512, wfmt="e2m1", act="bf16"),
     # the mid-M kernel with one expert per token (token index = assignment id)
     "w4a16_mid_k1": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=300, H=512, I=1024, E=4, k=1),
     # bf16 activations with I not a multiple of 256: the 16-row stream kernels
