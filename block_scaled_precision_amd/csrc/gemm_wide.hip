@@ -398,17 +398,6 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   return v;
 }
 
-// E4M3 codes of two values already divided by their block scale: nearest,
-// ties to even, saturating at 448.  The gfx950 conversion rounds to nearest
-// even (signed zeros kept) but turns magnitudes past 448 into NaN, hence the
-// clamp first; the scale operand 1.0 leaves the values as they are.
-typedef short v2s16 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  const v2s16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s16){0, 0}, a, b, 1.0f, false);
-  return (uint32_t)(uint16_t)r[0];
-}
 
 // ------------------------------------------------------------ multiply ---
 

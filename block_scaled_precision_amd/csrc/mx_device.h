@@ -79,6 +79,19 @@ __device__ __forceinline__ uint32_t encode(float q) {
   return code | sign;
 }
 
+// E4M3 codes (bytes 0 and 1) of two values already divided by their block
+// scale, by the hardware conversion: nearest, ties to even, signed zeros kept,
+// the same as encode<3>; the conversion turns magnitudes past 448 into NaN
+// instead of saturating, hence the clamp first.  The scale operand 1.0 leaves
+// the values as they are.
+typedef short v2s16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  const v2s16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s16){0, 0}, a, b, 1.0f, false);
+  return (uint32_t)(uint16_t)r[0];
+}
+
 // SiLU(g) * u in fp32.
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 

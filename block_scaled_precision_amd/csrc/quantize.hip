@@ -88,11 +88,13 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ src, 
       o[0] = make_uint2(w[0], w[1]);
       o[1] = make_uint2(w[2], w[3]);
       o[2] = make_uint2(w[4], w[5]);
-    } else {  // 32 bytes
+    } else {  // 32 bytes, two codes per hardware conversion
       uint32_t w[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        w[q] = c[4 * q] | (c[4 * q + 1] << 8) | (c[4 * q + 2] << 16) | (c[4 * q + 3] << 24);
+      for (int q = 0; q < 8; ++q) {
+        w[q] = e4m3_pair(__uint_as_float(v[4 * q]) * inv, __uint_as_float(v[4 * q + 1]) * inv) |
+               (e4m3_pair(__uint_as_float(v[4 * q + 2]) * inv, __uint_as_float(v[4 * q + 3]) * inv) << 16);
+      }
       uint4* o = (uint4*)(codes + i * 32);
       o[0] = make_uint4(w[0], w[1], w[2], w[3]);
       o[1] = make_uint4(w[4], w[5], w[6], w[7]);

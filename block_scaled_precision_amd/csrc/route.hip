@@ -127,12 +127,21 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   __shared__ int32_t s_a[kMaxExperts];
   __shared__ int32_t s_b[kMaxExperts];
   const int e = threadIdx.x;
+  // exclusive prefix of expert e's counts over the token blocks, 16 blocks
+  // per batch: all loads of a batch go out before its stores, so the walk
+  // costs one memory latency per 16 blocks instead of one per block
+  constexpr int kBatch = 16;
   int32_t count = 0;
   if (e < L) {
-    for (int b = 0; b < nblk; ++b) {
-      const int32_t h = hist[(int64_t)b * L + e];
-      hist[(int64_t)b * L + e] = count;
-      count += h;
+    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+      int32_t h[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) h[i] = b0 + i < nblk ? hist[(int64_t)(b0 + i) * L + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (b0 + i < nblk) hist[(int64_t)(b0 + i) * L + e] = count;
+        count += h[i];
+      }
     }
   }
   const int32_t ntile = (e < L && bm > 0) ? (count + bm - 1) / bm : 0;
@@ -153,7 +162,14 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   if (e < L) {
     offsets[e] = start;
     if (e == L - 1) offsets[L] = s_a[e];
-    for (int b = 0; b < nblk; ++b) hist[(int64_t)b * L + e] += start;
+    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
+      int32_t h[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) h[i] = b0 + i < nblk ? hist[(int64_t)(b0 + i) * L + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (b0 + i < nblk) hist[(int64_t)(b0 + i) * L + e] = h[i] + start;
+    }
     for (int i = 0; i < ntile; ++i) {
       const int32_t r0 = i * bm;
       Tile tl;
