@@ -74,6 +74,13 @@ __device__ __forceinline__ void add_bf16x8(float (&s)[8], uint4 v) {
     s[2 * q + 1] += __uint_as_float(w[q] & 0xffff0000u);
   }
 }
+constexpr int kCombineBatch = 8;  // slots in flight per thread
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte load that need not stay in the caches (the data is read once)
+__device__ __forceinline__ uint4 load_once(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ obuf, const uint4* __restrict__ sbuf,
                                                  const int32_t* __restrict__ ids, int k, int off, int L,
                                                  int H8, int64_t n8, uint4* __restrict__ y) {
@@ -82,18 +89,20 @@ __global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ obuf,
     const int64_t t = i / H8;
     const int64_t c = i - t * H8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < k; j0 += 4) {
-      uint4 v[4];
-      bool use[4];
+    // up to kCombineBatch slots in flight per thread; each obuf row is read
+    // once, so the loads bypass the caches' retention (non-temporal)
+    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+      uint4 v[kCombineBatch];
+      bool use[kCombineBatch];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kCombineBatch; ++q) {
         const int j = j0 + q < k ? j0 + q : j0;
         const int e = ids[t * k + j] - off;
         use[q] = j0 + q < k && e >= 0 && e < L;
-        v[q] = obuf[(t * k + j) * H8 + c];
+        v[q] = load_once(obuf + (t * k + j) * H8 + c);
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < kCombineBatch; ++q)
         if (use[q]) add_bf16x8(s, v[q]);
     }
     if (sbuf) add_bf16x8(s, sbuf[i]);
