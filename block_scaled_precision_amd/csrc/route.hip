@@ -31,15 +31,32 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
+// max of v with the value DPP control `ctrl` brings from another lane of its row
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, true);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Maximum over the wave (all 64 lanes active), returned wave-uniform: within
+// each row of 16 lanes by DPP (pairs, quads, then rotations by 4 and 8), then
+// across the four rows by reading one lane of each.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64<0xb1>(v);   // quad_perm 1,0,3,2
+  v = dpp_max_u64<0x4e>(v);   // quad_perm 2,3,0,1
+  v = dpp_max_u64<0x124>(v);  // row_ror 4
+  v = dpp_max_u64<0x128>(v);  // row_ror 8
+  uint64_t m = 0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    m = o > m ? o : m;
   }
-  return v;
+  return m;
 }
 
 // 4 waves per block, one token per wave; E <= 1024 -> at most 16 logits per lane.
@@ -59,32 +76,45 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
     const int e = lane + 64 * i;
     key[i] = e < E ? ordered_bits(row[e]) : 0u;
   }
+  // lane j keeps the id and logit of slot j (k <= E <= 1024, so slots past
+  // 63 are kept by lane j % 64 in round j / 64)
   float top = 0.f, sum = 0.f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+  for (int j0 = 0; j0 < k; j0 += 64) {
+    int my_e = 0;
+    float my_v = 0.f;
+    const int jn = min(k - j0, 64);
+    for (int jj = 0; jj < jn; ++jj) {
+      uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !(taken >> i & 1u)) {
-        const uint64_t kk = ((uint64_t)key[i] << 32) | (uint32_t)(kMaxExperts - 1 - e);
-        best = kk > best ? kk : best;
+      for (int i = 0; i < 16; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !(taken >> i & 1u)) {
+          const uint64_t kk = ((uint64_t)key[i] << 32) | (uint32_t)(kMaxExperts - 1 - e);
+          best = kk > best ? kk : best;
+        }
+      }
+      best = wave_max_u64(best);
+      const int e = kMaxExperts - 1 - (int)(best & 0xffffffffu);
+      const float v = from_ordered((uint32_t)(best >> 32));
+      if (j0 + jj == 0) top = v;
+      sum += expf(v - top);
+      if ((e & 63) == lane) taken |= 1u << (e >> 6);
+      if (lane == jj) {
+        my_e = e;
+        my_v = v;
       }
     }
-    best = wave_max_u64(best);
-    const int e = kMaxExperts - 1 - (int)(best & 0xffffffffu);
-    const float v = from_ordered((uint32_t)(best >> 32));
-    if (j == 0) top = v;
-    sum += expf(v - top);
-    if ((e & 63) == lane) taken |= 1u << (e >> 6);
-    if (lane == 0) {
-      ids[(int64_t)t * k + j] = e;
-      wts[(int64_t)t * k + j] = v;
+    if (lane < jn) ids[(int64_t)t * k + j0 + lane] = my_e;
+    if (k <= 64) {
+      // one batch: the sum is complete, the slot's logit is still in a register
+      if (lane < jn) wts[(int64_t)t * k + lane] = expf(my_v - top) * (1.0f / sum);
+      return;
     }
+    // the weights need the full sum: park the logits, normalised below
+    if (lane < jn) wts[(int64_t)t * k + j0 + lane] = my_v;
   }
-  if (lane == 0) {
-    const float inv = 1.0f / sum;
-    for (int j = 0; j < k; ++j) wts[(int64_t)t * k + j] = expf(wts[(int64_t)t * k + j] - top) * inv;
-  }
+  const float inv = 1.0f / sum;
+  for (int j = lane; j < k; j += 64) wts[(int64_t)t * k + j] = expf(wts[(int64_t)t * k + j] - top) * inv;
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
