@@ -187,19 +187,6 @@ __device__ __forceinline__ void copy_table(const FcArgs& p, const ItemGeom& it, 
   }
 }
 
-// s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n in [LO, HI] (binary search
-// over the immediate forms; n above HI waits for HI, which is stricter).
-template <int LO, int HI>
-__device__ __forceinline__ void wait_ops(int n) {
-  if constexpr (LO == HI) {
-    wait_vm_lgkm0<LO>();
-  } else {
-    constexpr int MID = (LO + HI + 1) / 2;
-    if (n >= MID) wait_ops<MID, HI>(n);
-    else wait_ops<LO, MID - 1>(n);
-  }
-}
-
 // Memory-counter bookkeeping of a copy stream in closed form.  A wave issues
 // its prologue (code stages 0..NS-1, C copies each, then scale groups 0 and
 // 1, one copy each) and after barrier g the code stage of step g+NS and, when
@@ -212,23 +199,40 @@ template <int NS, int C>
 struct CopyCount {
   static constexpr int P = NS * C + 2;
   // copies issued before barrier g
-  static __device__ __forceinline__ int before(int g) { return P + g * C + g / kGroup; }
+  static constexpr int before(int g) { return P + g * C + g / kGroup; }
   // copies issued up to and including code stage s / scale group G
-  static __device__ __forceinline__ int code_end(int s) {
+  static constexpr int code_end(int s) {
     return s < NS ? (s + 1) * C : P + (s - NS + 1) * C + (s - NS) / kGroup;
   }
-  static __device__ __forceinline__ int group_end(int G) {
+  static constexpr int group_end(int G) {
     return G < 2 ? NS * C + G + 1 : P + (kGroup * G - kGroup) * C + (G - 2) + 1;
   }
-  // before barrier g: the code stage of step g+1 has landed and, when step g+1
-  // opens a scale group, that group too
+  // copies that may stay in flight before barrier g: all but those up to the
+  // code stage of step g+1 and, when step g+1 opens a scale group, that group
+  static constexpr int allowed(int g) {
+    const int ce = code_end(g + 1);
+    const int need = ((g + 1) % kGroup) == 0 ? (ce > group_end((g + 1) / kGroup) ? ce : group_end((g + 1) / kGroup)) : ce;
+    return before(g) - need;
+  }
+  // From step kGroup on, allowed(g) depends only on g % kGroup; over the first
+  // steps it is larger.  So the steady-state value of g's phase is never looser
+  // than the exact count, and each wait is a compile-time immediate.
+  static constexpr int steady(int q) { return allowed(4 * kGroup + q); }
+  static constexpr bool steady_is_safe() {
+    for (int g = 0; g < 8 * kGroup; ++g)
+      if (steady(g % kGroup) > allowed(g)) return false;
+    return true;
+  }
+  static_assert(kGroup == 4 && steady_is_safe(), "per-phase waits");
   static __device__ __forceinline__ void wait_step(int g) {
-    int need = code_end(g + 1);
-    if (((g + 1) & (kGroup - 1)) == 0) need = max(need, group_end((g + 1) / kGroup));
-    wait_ops<0, NS * C + 2>(before(g) - need);
+    switch (g & (kGroup - 1)) {
+      case 0: wait_vm_lgkm0<steady(0)>(); break;
+      case 1: wait_vm_lgkm0<steady(1)>(); break;
+      case 2: wait_vm_lgkm0<steady(2)>(); break;
+      default: wait_vm_lgkm0<steady(3)>(); break;
+    }
   }
 };
-
 // The activation stream of wave (wm, 0): codes of rows [48 wm, 48 wm + 48)
 // (1-KB copy t = 6 wm + i holds rows 8t .. 8t+7, lane -> row 8t + lane/8,
 // slot lane%8 receiving chunk (lane%8) ^ (row%8)), scale groups of rows
