@@ -245,6 +245,13 @@ struct ACopier {
   using Count = CopyCount<kAStages, kACodeCopies>;
   uint32_t src[kACodeCopies];  // FC1 routed: byte offsets into the activations (< 4 GiB)
   int nb, p0, rows;            // the code cursor's item
+  // Both streams advance one code stage / one scale group per call, so their
+  // (item, step) cursors are counted instead of divided out of the step index.
+  int cli = 0, cls = 0;        // code cursor: item, step within it
+  int gli = 0, gls = 0;        // scale-group cursor: item, first step of the group
+  int gitem = -1;              // item whose group source offsets are held below
+  uint32_t goff;               // per-lane scale-row offset of that item
+  int gnb;
   // FC1 gathers token rows through the row table (or, dense, rows p0 + r), and
   // keeps the per-lane row offsets for the item; FC2's tile row r is always
   // activation row p0 + r, so its offsets are recomputed at each issue (no
@@ -266,7 +273,11 @@ struct ACopier {
     if (s >= sc.total) return;
     const int lane = threadIdx.x & 63;
     const uint32_t lds0 = lds_addr(smem);
-    const int li = s / sc.nk, ls = s - li * sc.nk;
+    const int li = cli, ls = cls;
+    if (++cls == sc.nk) {
+      cls = 0;
+      ++cli;
+    }
     if (ls == 0) {
       // the next item's table goes out before this item's first stage
       if (p.dense_rows == 0 && li + 1 < sc.my_items)
@@ -301,13 +312,23 @@ struct ACopier {
   // scale group G (steps 4G .. 4G+3)
   __device__ __forceinline__ void issue_group(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int G) {
     if (kGroup * G >= sc.total) return;
-    const int lane = threadIdx.x & 63;
-    const int li = kGroup * G / sc.nk, ls = kGroup * G - li * sc.nk;
-    const ItemGeom it = item_geom(p, sc, li);
+    const int li = gli, ls = gls;
+    gls += kGroup;
+    if (gls == sc.nk) {
+      gls = 0;
+      ++gli;
+    }
     const int u = min(wm, TBM / 64 - 1);
-    const uint32_t off = src_row(p, smem, it, li, 64 * u + lane) * (uint32_t)(p.K / 32);
-    lds_copy16_s(p.a_scale + 4 * k_step(sc, it.nb, ls), off,
-                 lds_addr(smem) + L_AS + (G % 2) * AS_GROUP + 1024 * u);
+    if (li != gitem) {
+      // a new item: its rows' scale offsets (the item's row table has landed:
+      // it went out before the item's first code stage, which precedes this)
+      const int lane = threadIdx.x & 63;
+      const ItemGeom it = item_geom(p, sc, li);
+      goff = src_row(p, smem, it, li, 64 * u + lane) * (uint32_t)(p.K / 32);
+      gnb = it.nb;
+      gitem = li;
+    }
+    lds_copy16_s(p.a_scale + 4 * k_step(sc, gnb, ls), goff, lds_addr(smem) + L_AS + (G % 2) * AS_GROUP + 1024 * u);
   }
 
   __device__ __forceinline__ void prologue(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm) {
@@ -334,6 +355,10 @@ template <bool FC1>
 struct BCopier {
   using Count = CopyCount<kBStages, kBCodeCopies>;
   int nb, expert;  // of the code cursor's item; per-lane offsets are recomputed at each issue
+  int cli = 0, cls = 0;  // code cursor: item, step within it (counted, as in ACopier)
+  int gli = 0, gls = 0;  // scale-group cursor
+  int gitem = -1;        // item whose scale-row base is held in gbase
+  const uint8_t* gbase;
 
   // First weight row of the wave's 64 B-tile rows [64 wm, 64 wm + 64): FC1 takes
   // gate rows (even wm) or the matching up rows (odd wm) of h columns
@@ -346,7 +371,11 @@ struct BCopier {
   __device__ __forceinline__ void issue_code(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int s) {
     if (s >= sc.total) return;
     const int lane = threadIdx.x & 63;
-    const int li = s / sc.nk, ls = s - li * sc.nk;
+    const int li = cli, ls = cls;
+    if (++cls == sc.nk) {
+      cls = 0;
+      ++cli;
+    }
     if (ls == 0) {
       const ItemGeom it = item_geom(p, sc, li);
       nb = it.nb;
@@ -366,11 +395,18 @@ struct BCopier {
   __device__ __forceinline__ void issue_group(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm, int G) {
     if (kGroup * G >= sc.total) return;
     const int lane = threadIdx.x & 63;
-    const int li = kGroup * G / sc.nk, ls = kGroup * G - li * sc.nk;
-    const ItemGeom it = item_geom(p, sc, li);
-    const uint8_t* sw =
-        p.w_scale + (int64_t)it.expert * p.ws_estride + row0(p, it.nb, wm) * (p.K / 32) + 4 * k_step(sc, it.nb, ls);
-    lds_copy16_s(sw, (uint32_t)lane * (uint32_t)(p.K / 32), lds_addr(smem) + L_BS + (G % 2) * BS_GROUP + 1024 * wm);
+    const int li = gli, ls = gls;
+    gls += kGroup;
+    if (gls == sc.nk) {
+      gls = 0;
+      ++gli;
+    }
+    if (li != gitem) {
+      const ItemGeom it = item_geom(p, sc, li);
+      gbase = p.w_scale + (int64_t)it.expert * p.ws_estride + row0(p, it.nb, wm) * (p.K / 32);
+      gitem = li;
+    }
+    lds_copy16_s(gbase + 4 * ls, (uint32_t)lane * (uint32_t)(p.K / 32), lds_addr(smem) + L_BS + (G % 2) * BS_GROUP + 1024 * wm);
   }
 
   __device__ __forceinline__ void prologue(const FcArgs& p, const Sched& sc, const uint8_t* smem, int wm) {
