@@ -192,9 +192,17 @@ __device__ __forceinline__ void copy_table(const FcArgs& p, const ItemGeom& it, 
 // 1, one copy each) and after barrier g the code stage of step g+NS and, when
 // g % 4 == 3, scale group (g+1)/4 + 1.  Row-table copies are left out of the
 // count: they only add to the copies in flight after a given one, so leaving
-// them out makes a wait stricter, never looser; stages or groups past the end
-// are left out of the issue but not of the count, which again only makes the
-// waits stricter.
+// them out makes a wait stricter, never looser.  Stages or groups past the end
+// of the stream are not issued but are counted, which would make a wait
+// looser (copies complete in issue order, so a wait that assumes more younger
+// copies than exist can pass before the one it guards); the last waits of a
+// stream, from barrier total - kTailWaits on, therefore wait for every copy.
+// barriers at the end of a stream whose waits could count a skipped copy: a
+// code stage is skipped from barrier total - NS on (NS <= 4), a scale group
+// from barrier total - 5 on
+constexpr int kTailWaits = 5;
+static_assert(kTailWaits >= kAStages - 1 && kTailWaits >= kBStages - 1 && kGroup + 1 <= kTailWaits, "tail waits");
+
 template <int NS, int C>
 struct CopyCount {
   static constexpr int P = NS * C + 2;
@@ -518,8 +526,8 @@ __device__ __forceinline__ void item_steps(const FcArgs& p, const Sched& sc, v4f
                                            const LaneOffs& o, uint8_t* smem, Copier& cp, int wm, int gbase) {
   for (int s = 0; s < sc.nk; ++s) {
     const int g = gbase + s;
-    if (g + 1 < sc.total) cp.wait_for(g);
-    else wait_lgkm0();
+    if (g + kTailWaits < sc.total) cp.wait_for(g);
+    else wait_vm_lgkm0<0>();
     barrier();
     cp.issue(p, sc, smem, wm, g);
     const int nx = g + 1;
