@@ -188,9 +188,14 @@ static FusedPlan plan(const moe_problem_t& p) {
     // E2M1 weights take the wide tiled kernel (256-row weight blocks)
     // (K a multiple of 512 and at least 1024: scale groups of 4 K-steps, items
     // of at least 8 steps)
-    const bool wide_h = p.w_fmt == MX_E2M1 && p.H % 512 == 0 && p.H >= 1024;
-    const bool wide = tiled && wide_h && p.I % 512 == 0 && p.I >= 1024 && kdiv_ok;
-    const bool shared_wide = shared_tiled && wide_h && p.I_shared % 512 == 0 && p.I_shared >= 1024;
+    // The wide kernel addresses activation rows by 32-bit byte offsets from
+    // the operand's base: token * H for FC1 (x codes), permuted row * I for FC2
+    // (h codes), which must stay below 4 GiB.
+    const double lim = 4294967296.0;
+    const bool wide_h = p.w_fmt == MX_E2M1 && p.H % 512 == 0 && p.H >= 1024 && (double)p.T * p.H < lim;
+    const bool wide = tiled && wide_h && p.I % 512 == 0 && p.I >= 1024 && kdiv_ok && (double)f.A * p.I < lim;
+    const bool shared_wide = shared_tiled && wide_h && p.I_shared % 512 == 0 && p.I_shared >= 1024 &&
+                             (double)p.T * p.I_shared < lim;
     f.routed = wide ? Fc::kWide : (tiled ? Fc::kTiled : Fc::kStream);
     f.shared = shared_wide ? Fc::kWide : (shared_tiled ? Fc::kTiled : Fc::kStream);
   } else {
