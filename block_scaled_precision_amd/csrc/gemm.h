@@ -53,12 +53,13 @@ hipError_t launch_fc_stream(const FcArgs& p, bool fc1, bool mx_act, int wfmt, hi
 // or kTiledRowsLow when experts see fewer rows: less LDS for activations, a
 // deeper weight ring), N-blocks of 64 h columns (FC1: nchunks = I / 64) or 128
 // output columns (FC2: nchunks = H / 128); `grid` persistent workgroups (rounded
-// down to a multiple of 8, at least 8).  Requires K >= kTiledMinK.
+// down to a multiple of 8, at least 8).  Requires K to be a multiple of
+// kTiledKMultiple (scales travel in groups of 4 128-K stages).
 constexpr int kTiledRows = 192;
 constexpr int kTiledRowsLow = 128;
 constexpr int kTiledColsFc1 = 64;
 constexpr int kTiledColsFc2 = 128;
-constexpr int kTiledMinK = 256;
+constexpr int kTiledKMultiple = 512;
 hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int rows, int grid, hipStream_t st);
 
 // Wide variant (MXFP8 activations x E2M1 weights): M-tiles of up to kTiledRows

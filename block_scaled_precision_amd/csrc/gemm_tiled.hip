@@ -23,12 +23,13 @@
 //    spreads over all SIMDs) and two 32-column MFMA tiles, reads its operands
 //    from LDS and writes the item's results;
 //  * waves 8-9 copy the activation stage (gathered rows of E4M3 codes, 128 B per
-//    row and stage, plus the per-row scale words) into a ring of 4 LDS
-//    buffers, three stages ahead of the multiply;
+//    row and stage) into a ring of 4 LDS buffers, three stages ahead of the
+//    multiply, and the rows' scale words in groups of 4 stages;
 //  * waves 10-11 copy the weight stage (64 B per row and stage for E2M1, 96 B
-//    for E3M2, plus scale words) into a deeper ring (with 192-row tiles 6
-//    buffers for E2M1, 4 for E3M2; with 128-row tiles 10 and 7) so that
-//    weights, which come from HBM, are requested further ahead.
+//    for E3M2) into a deeper ring (with 192-row tiles 6 buffers for E2M1, 4
+//    for E3M2; with 128-row tiles 10 and 7) so that weights, which come from
+//    HBM, are requested further ahead, and the rows' scale words in groups of
+//    4 stages.
 // The copies are global_load_lds (global memory straight into LDS) issued from
 // inline assembly; each copy wave waits for its own stage with an explicit
 // vmcnt before the barrier.  Because a wave's memory counter drains in order,
@@ -69,10 +70,15 @@ constexpr int kWaveA = kComputeWaves;      // first activation-copy wave
 constexpr int kWaveB = kComputeWaves + 2;  // first weight-copy wave
 constexpr int kGroupsM = kComputeWaves / 2;  // multiply waves along M
 
-// LDS layout: [A ring: STAGES x (codes TM x 128 B + scale words TM x 4 B)]
-//             [B ring: NBS x (weights + scale words 512 B)]
+// LDS layout: [A ring: STAGES x codes TM x 128 B] [B ring: NBS x weight codes]
+//             [A scale groups: 2 x TM x 16 B] [B scale groups: 2 x TBN x 16 B]
 //             [row tables: TABLES x (source row TM x 4 B + weight TM x 4 B)]
-// for M-tiles of TM rows (kTiledRows or kTiledRowsLow).
+// for M-tiles of TM rows (kTiledRows or kTiledRowsLow).  Scales travel in
+// groups of 4 stages: the 16 scale bytes of a row for 4 consecutive stages
+// are contiguous in both operands, so one 16-byte copy per row serves 4
+// stages (a 4-byte copy per row and stage costs one memory request per row
+// for 4 bytes, as many requests as the codes themselves).  K is a multiple of
+// 512, so an item's steps fill whole groups.
 template <int TM> struct ALay {
   static_assert(TM % 64 == 0 && TM <= 256, "tile rows");
   static constexpr int STAGES = 4;
@@ -83,55 +89,88 @@ template <int TM> struct ALay {
   static constexpr int TABLES = 4;
   static_assert((TABLES - 2) * 2 >= STAGES, "row table ring too short");
   static constexpr int MAX_SUB = (TM / 32 + kGroupsM - 1) / kGroupsM;  // 32-row sub-blocks per multiply wave
-  static constexpr int CODE_COPIES = TM / 16;  // 1-KB code copies per activation-copy wave
-  static constexpr int SCALE_COPIES = TM / 64; // 256-B scale copies in a stage (both waves)
-  static constexpr int CODES = TM * TBK;
-  static constexpr int STAGE = CODES + TM * 4;
+  static constexpr int CODE_COPIES = TM / 16;  // 1-KB code copies per activation-copy wave and stage
+  static constexpr int SCALE_CHUNKS = TM / 64;  // 1-KB copies (64 rows x 16 B) in a scale group
+  static constexpr int GROUP_COPIES = (SCALE_CHUNKS + 1) / 2;  // per activation-copy wave and group
+  static constexpr int STAGE = TM * TBK;
+  static constexpr int GROUP = TM * 16;
   static constexpr int TABLE = TM * 8;
-  static constexpr int COPIES = CODE_COPIES + 2;  // per copy wave and stage: codes + two scale copies
 };
 // The weight ring takes what the activation ring and the tables leave of the
 // LDS: with shorter M-tiles more weight stages (which come from HBM) are in
 // flight.
 template <int WF, int TM> struct BLay {
   static constexpr int ROW = WF == 1 ? 64 : 96;    // bytes of one weight row per stage
-  static constexpr int CODES = TBN * ROW;
-  static constexpr int STAGE = CODES + TBN * 4;
-  static constexpr int COPIES = CODES / 1024;      // 1-KB copies per stage: 8 or 12
+  static constexpr int STAGE = TBN * ROW;
+  static constexpr int COPIES = STAGE / 1024;      // 1-KB copies per stage: 8 or 12
   static constexpr int PER_WAVE = COPIES / 2;      // per weight-copy wave: 4 or 6
+  static constexpr int GROUP = TBN * 16;           // one 1-KB copy per weight-copy wave
   static constexpr int NBS = TM == kTiledRows ? (WF == 1 ? 6 : 4) : (WF == 1 ? 10 : 7);  // ring depth
-  static_assert((NBS - 2) * (PER_WAVE + 1) < 64, "vmcnt range");
 };
 template <int WF, int TM> struct Lds {
   static constexpr int A = 0;
   static constexpr int B = ALay<TM>::STAGES * ALay<TM>::STAGE;
-  static constexpr int TBL = B + BLay<WF, TM>::NBS * BLay<WF, TM>::STAGE;
+  static constexpr int AS = B + BLay<WF, TM>::NBS * BLay<WF, TM>::STAGE;
+  static constexpr int BS = AS + 2 * ALay<TM>::GROUP;
+  static constexpr int TBL = BS + 2 * BLay<WF, TM>::GROUP;
   static constexpr int TOTAL = TBL + ALay<TM>::TABLES * ALay<TM>::TABLE;
   static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
-template <int WF, int TM> constexpr int b_copies() { return BLay<WF, TM>::PER_WAVE + 1; }
+// Memory-counter bookkeeping of a copy wave with an NS-stage ring, C copies
+// per stage and GC per scale group, in closed form.  Issue order: the prologue
+// copies scale groups 0 and 1, then stages 0 .. NS-2; after barrier x the wave
+// copies group x/4 + 1 when x % 4 == 0 and x >= 4 (into the buffer of group
+// x/4 - 1, whose last stage was read before barrier x), then stage x + NS - 1.
+// Stages and groups past the end of the stream are not issued and not
+// counted.  Row-table copies are left out: they only add copies in flight
+// after a given one, so leaving them out makes a wait stricter.  The copy
+// waves do nothing else, so the counts are computed at run time.
+template <int NS, int C, int GC>
+struct CopyCount {
+  int total, ngroups;
+  // copies issued through the slot after barrier x (x = -1: the prologue)
+  __device__ __forceinline__ int issued_through(int x) const {
+    return C * min(total, NS + x) + GC * min(ngroups, x >= 4 ? 2 + x / 4 : 2);
+  }
+  // copies issued up to and including stage s (issued in slot s - NS + 1,
+  // after that slot's group)
+  __device__ __forceinline__ int through_stage(int s) const {
+    const int x = s - NS + 1;
+    return C * (s + 1) + GC * min(ngroups, x >= 4 ? 2 + x / 4 : 2);
+  }
+  // copies issued up to and including group G (issued in slot 4G - 4, before
+  // that slot's stage; groups 0 and 1 open the prologue)
+  __device__ __forceinline__ int through_group(int G) const {
+    if (G < 2) return GC * (G + 1);
+    return C * min(total, NS + 4 * G - 5) + GC * (G + 1);
+  }
+  // copies that may stay in flight before barrier b: all but those up to
+  // stage b and, when b opens a group, that group
+  __device__ __forceinline__ int allowed(int b) const {
+    int need = through_stage(b);
+    if ((b & 3) == 0) need = max(need, through_group(b >> 2));
+    return issued_through(b - 1) - need;
+  }
+};
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n in [LO, HI] (a compare ladder)
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vm_lgkm0<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vm_range<LO, MID>(n);
+    else wait_vm_range<MID + 1, HI>(n);
+  }
+}
 
 // A tile: row r holds 8 chunks of 16 B; chunk c sits at slot c ^ (r & 7) so
 // that 8 consecutive rows read at the same k land in 8 different bank groups.
 __device__ __forceinline__ int a_off(int r, int c) { return r * TBK + 16 * (c ^ (r & 7)); }
 // E2M1 B tile: 4 chunks per 64-B row, chunk c at slot c ^ ((r >> 1) & 3).
 __device__ __forceinline__ int b4_off(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 1) & 3)); }
-
-// at most n (<= N) stages of COPIES copies each may stay in flight (copies
-// issued before them, such as row tables, are waited for as well)
-template <int COPIES, int N>
-__device__ __forceinline__ void wait_stages(int n) {
-  if constexpr (N > 0) {
-    if (n >= N) {
-      wait_vm_lgkm0<N * COPIES>();
-      return;
-    }
-    wait_stages<COPIES, N - 1>(n);
-  } else {
-    wait_vm_lgkm0<0>();
-  }
-}
 
 struct ItemGeom {
   int expert, p0, rows, nb;
@@ -175,9 +214,11 @@ __device__ __forceinline__ ItemGeom item_geom(const FcArgs& p, const Sched& sc, 
 // same time on one XCD and read the same activation rows; starting each at a
 // different K stage (rotated by its N-block index) means only the first to
 // reach a stage misses in L2 and the others hit, instead of all of them
-// waiting on the same miss.  The multiply is indifferent to the K order.
+// waiting on the same miss.  The multiply is indifferent to the K order.  The
+// rotation is a multiple of 4 stages, so a scale group's 4 steps are 4
+// consecutive stages starting at a multiple of 4.
 __device__ __forceinline__ int k_stage(const Sched& sc, int nb, int ls) {
-  const int s = ls + nb * sc.nk / sc.NB;
+  const int s = ls + ((nb * sc.nk / sc.NB) & ~3);
   return s < sc.nk ? s : s - sc.nk;
 }
 
@@ -191,14 +232,14 @@ __device__ __forceinline__ int64_t w_row(const FcArgs& p, int nb, int jr) {
 // ------------------------------------------------------------ multiply ---
 
 // One 128-K stage for a wave holding NM (1 to kMaxSub) sub-blocks: sub-block
-// wm + kGroupsM*m of the tile times the wave's two 32-column B tiles.
+// wm + kGroupsM*m of the tile times the wave's two 32-column B tiles.  `ags`
+// and `bgs` point at the stage's scale words in its scale group buffers (row
+// r's word at 16 r).
 template <int WF, int TM, int NM>
 __device__ __forceinline__ void compute_stage(v16f (&acc)[ALay<TM>::MAX_SUB][2], const uint8_t* as, const uint8_t* bs,
-                                              int wm, int brow0, int brow1) {
+                                              const uint8_t* ags, const uint8_t* bgs, int wm, int brow0, int brow1) {
   using BL = BLay<WF, TM>;
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
-  const uint32_t* SAs = (const uint32_t*)(as + ALay<TM>::CODES);
-  const uint32_t* SBs = (const uint32_t*)(bs + BL::CODES);
   v8i bv[2][2];
   uint32_t bsw[2];
   v8i av[2][NM];
@@ -206,7 +247,7 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[ALay<TM>::MAX_SUB][2],
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int jr = (n == 0 ? brow0 : brow1) + l32;
-    bsw[n] = SBs[jr];
+    bsw[n] = *(const uint32_t*)(bgs + 16 * jr);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int blk = 2 * kk + g;
@@ -230,7 +271,7 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[ALay<TM>::MAX_SUB][2],
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     const int r = 32 * (wm + kGroupsM * m) + l32;
-    asw[m] = SAs[r];
+    asw[m] = *(const uint32_t*)(ags + 16 * r);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const uint4 lo = *(const uint4*)(as + a_off(r, 4 * kk + g));
@@ -290,11 +331,14 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
     barrier();
     const uint8_t* as = smem + L::A + (gidx % AL::STAGES) * AL::STAGE;
     const uint8_t* bs = smem + L::B + (gidx % BL::NBS) * BL::STAGE;
+    const int gb = (gidx >> 2) & 1, q = gidx & 3;
+    const uint8_t* ags = smem + L::AS + gb * AL::GROUP + 4 * q;
+    const uint8_t* bgs = smem + L::BS + gb * BL::GROUP + 4 * q;
     switch (nm) {
-      case 4: if constexpr (kMaxSub >= 4) compute_stage<WF, TM, 4>(acc, as, bs, wm, brow0, brow1); break;
-      case 3: if constexpr (kMaxSub >= 3) compute_stage<WF, TM, 3>(acc, as, bs, wm, brow0, brow1); break;
-      case 2: if constexpr (kMaxSub >= 2) compute_stage<WF, TM, 2>(acc, as, bs, wm, brow0, brow1); break;
-      case 1: compute_stage<WF, TM, 1>(acc, as, bs, wm, brow0, brow1); break;
+      case 4: if constexpr (kMaxSub >= 4) compute_stage<WF, TM, 4>(acc, as, bs, ags, bgs, wm, brow0, brow1); break;
+      case 3: if constexpr (kMaxSub >= 3) compute_stage<WF, TM, 3>(acc, as, bs, ags, bgs, wm, brow0, brow1); break;
+      case 2: if constexpr (kMaxSub >= 2) compute_stage<WF, TM, 2>(acc, as, bs, ags, bgs, wm, brow0, brow1); break;
+      case 1: compute_stage<WF, TM, 1>(acc, as, bs, ags, bgs, wm, brow0, brow1); break;
       default: break;
     }
     if (++cs < sc.nk) continue;
@@ -380,102 +424,116 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
   using L = Lds<WF, TM>;
   using AL = ALay<TM>;
   constexpr int kACodeCopies = AL::CODE_COPIES;
-  constexpr int kAScaleCopies = AL::SCALE_COPIES;
-  constexpr int kACopies = AL::COPIES;
+  constexpr int kGC = AL::GROUP_COPIES;
+  constexpr int kMaxWait = (AL::STAGES - 1) * kACodeCopies + 2 * kGC;
+  static_assert(kMaxWait < 64, "vmcnt range");
   const int lane = threadIdx.x & 63, aw = (threadIdx.x >> 6) - kWaveA;
   const int K = p.K;
   const bool routed = p.dense_rows == 0;
   const uint32_t lds0 = lds_addr(smem);
   const int c = (lane & 7) ^ (lane >> 3);  // chunk that lands in this lane's LDS slot
+  const CopyCount<AL::STAGES, kACodeCopies, kGC> cnt{sc.total, sc.total / 4};
+
+  // activation row (token for FC1, permuted row for FC2) of tile row r of
+  // item li, whose row table must have landed
+  auto src_row = [&](const ItemGeom& it, int li, int r) -> int64_t {
+    r = r < it.rows ? r : it.rows - 1;  // rows past the tile repeat its last row
+    if (!routed) return it.p0 + r;
+    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (li % AL::TABLES) * AL::TABLE);
+    return FC1 ? tsrc[r] / p.k : (int64_t)it.p0 + r;
+  };
 
   const uint8_t* asrc[kACodeCopies];
-  const uint8_t* ssrc[2];
   int load_nb = 0;
-  // source rows of item li; its row table must have landed
-  auto setup = [&](int li) {
-    const ItemGeom it = item_geom<TM>(p, sc, li);
-    load_nb = it.nb;
-    const int32_t* tsrc = (const int32_t*)(smem + L::TBL + (li % AL::TABLES) * AL::TABLE);
-    auto src_row = [&](int r) -> int64_t {
-      r = r < it.rows ? r : it.rows - 1;  // rows past the tile repeat its last row
-      if (!routed) return it.p0 + r;
-      return FC1 ? tsrc[r] / p.k : (int64_t)it.p0 + r;
-    };
-#pragma unroll
-    for (int i = 0; i < kACodeCopies; ++i) {
-      const int t = kACodeCopies * aw + i;
-      asrc[i] = (const uint8_t*)p.a + src_row(8 * t + (lane >> 3)) * K + 16 * c;
-    }
-    // scale copies: wave 0 takes 0, 1 and wave 1 takes 2, 3 (a missing one
-    // repeats the last: the same bytes to the same place)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) ssrc[i] = p.a_scale + src_row(64 * min(2 * aw + i, kAScaleCopies - 1) + lane) * (K / 32);
-  };
-  auto issue = [&](int s, int buf) {
-    const uint32_t base = lds0 + L::A + buf * AL::STAGE;
-#pragma unroll
-    for (int i = 0; i < kACodeCopies; ++i) lds_copy16(asrc[i] + s * TBK, base + 1024 * (kACodeCopies * aw + i));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      lds_copy4(ssrc[i] + 4 * s, base + AL::CODES + 256 * min(2 * aw + i, kAScaleCopies - 1));
-  };
-
-  // load cursor: item li, stage ls; stages issued so far
-  int li = 0, ls = 0, issued = 0;
-  if (routed) {
-    copy_table<TM>(p, item_geom<TM>(p, sc, 0), lds0 + L::TBL);
-    wait_vm_lgkm0<0>();
-  }
-  // issue the next stage; at the start of an item, first copy the next item's
-  // row table (these copies are older than the stage's, so the per-step wait
-  // below also covers them)
-  auto issue_next = [&]() {
+  int li = 0, ls = 0, issued = 0;  // code cursor: item, step within it; stages issued
+  int gli = 0, gls = 0;            // group cursor: item, first step of the group
+  const uint8_t* gsrc[kGC];        // the group cursor's item: per-lane scale rows
+  int gnb = 0;
+  // the next code stage; at the start of an item, first copy the row table of
+  // the item after it (older than the stage's copies, so the wait for the
+  // stage covers it; tables 0 and 1 go out in the prologue)
+  auto issue_stage = [&]() {
     if (ls == 0) {
-      if (routed && li + 1 < sc.my_items)
+      if (routed && li > 0 && li + 1 < sc.my_items)
         copy_table<TM>(p, item_geom<TM>(p, sc, li + 1), lds0 + L::TBL + ((li + 1) % AL::TABLES) * AL::TABLE);
-      setup(li);
+      // item li's table went out with the first stage of item li-1, at least
+      // nk >= STAGES - 1 stages before the one the last wait covered
+      const ItemGeom it = item_geom<TM>(p, sc, li);
+      load_nb = it.nb;
+#pragma unroll
+      for (int i = 0; i < kACodeCopies; ++i)
+        asrc[i] = (const uint8_t*)p.a + src_row(it, li, 8 * (kACodeCopies * aw + i) + (lane >> 3)) * K + 16 * c;
     }
-    issue(k_stage(sc, load_nb, ls), issued % AL::STAGES);
+    const int ks = k_stage(sc, load_nb, ls);
+    const uint32_t base = lds0 + L::A + (issued % AL::STAGES) * AL::STAGE;
+#pragma unroll
+    for (int i = 0; i < kACodeCopies; ++i) lds_copy16(asrc[i] + ks * TBK, base + 1024 * (kACodeCopies * aw + i));
     ++issued;
     if (++ls == sc.nk) {
       ls = 0;
       ++li;
-      // the next setup reads item li's table, copied before the stage just
-      // issued: waiting until at most one stage of copies is in flight
-      // guarantees it has landed
-      if (li < sc.my_items) wait_vm_lgkm0<kACopies>();
     }
   };
-  for (int s = 0; s < AL::STAGES - 1 && s < sc.total; ++s) issue_next();
+  // scale group G: 16 bytes per row (the 4 stages from the group's first K
+  // stage) in 64-row chunks; wave aw copies chunks kGC*aw .. kGC*aw + kGC - 1
+  // (a missing one repeats the last: the same bytes to the same place).  The
+  // group opening item li is copied 4 steps before it, after the wait that
+  // covers the stage copied with item li's row table.
+  auto issue_group = [&](int G) {
+    if (gls == 0) {
+      const ItemGeom it = item_geom<TM>(p, sc, gli);
+      gnb = it.nb;
+#pragma unroll
+      for (int i = 0; i < kGC; ++i)
+        gsrc[i] = p.a_scale + src_row(it, gli, 64 * min(kGC * aw + i, AL::SCALE_CHUNKS - 1) + lane) * (K / 32);
+    }
+    const int ks = k_stage(sc, gnb, gls);
+    const uint32_t base = lds0 + L::AS + (G & 1) * AL::GROUP;
+#pragma unroll
+    for (int i = 0; i < kGC; ++i)
+      lds_copy16(gsrc[i] + 4 * ks, base + 1024 * min(kGC * aw + i, AL::SCALE_CHUNKS - 1));
+    gls += 4;
+    if (gls == sc.nk) {
+      gls = 0;
+      ++gli;
+    }
+  };
+
+  if (routed) {
+    copy_table<TM>(p, item_geom<TM>(p, sc, 0), lds0 + L::TBL);
+    if (sc.my_items > 1) copy_table<TM>(p, item_geom<TM>(p, sc, 1), lds0 + L::TBL + AL::TABLE);
+    wait_vm_lgkm0<0>();
+  }
+  for (int G = 0; G < 2 && G < cnt.ngroups; ++G) issue_group(G);
+  for (int s = 0; s < AL::STAGES - 1 && s < sc.total; ++s) issue_stage();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
-    // stage gidx has landed once at most the stages issued after it remain
-    wait_stages<kACopies, AL::STAGES - 2>(issued - 1 - gidx);
+    wait_vm_range<0, kMaxWait>(min(cnt.allowed(gidx), kMaxWait));
     barrier();
-    if (issued < sc.total) issue_next();
+    if (gidx >= 4 && (gidx & 3) == 0 && (gidx >> 2) + 1 < cnt.ngroups) issue_group((gidx >> 2) + 1);
+    if (issued < sc.total) issue_stage();
   }
 }
 
 // --------------------------------------------------------- weight copies ---
 
-
-
 template <bool FC1, int WF, int TM>
 __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
   using L = Lds<WF, TM>;
   using BL = BLay<WF, TM>;
+  constexpr int kMaxWait = (BL::NBS - 1) * BL::PER_WAVE + 2;
+  static_assert(kMaxWait < 64, "vmcnt range");
   const int lane = threadIdx.x & 63, bw = (threadIdx.x >> 6) - kWaveB;
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
   const int64_t wrow = (int64_t)K * Fmt<WF>::BITS / 8;
+  const CopyCount<BL::NBS, BL::PER_WAVE, 1> cnt{sc.total, sc.total / 4};
 
   const uint8_t* bsrc[BL::PER_WAVE];
-  const uint8_t* ssrc;
   int load_nb = 0;
   auto setup = [&](int li) {
     const ItemGeom it = item_geom<TM>(p, sc, li);
     load_nb = it.nb;
     const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride;
-    const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride;
 #pragma unroll
     for (int i = 0; i < BL::PER_WAVE; ++i) {
       const int t = BL::PER_WAVE * bw + i;  // 1-KB copy index within the stage
@@ -490,29 +548,45 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
       }
       bsrc[i] = wb + w_row<FC1>(p, it.nb, jr) * wrow + 16 * ch;
     }
-    ssrc = sb + w_row<FC1>(p, it.nb, 64 * bw + lane) * (K / 32);
   };
-  int li = 0, ls = 0, issued = 0;
-  auto issue_next = [&]() {
+  int li = 0, ls = 0, issued = 0;  // code cursor
+  int gli = 0, gls = 0;            // group cursor
+  const uint8_t* gsrc = nullptr;   // the group cursor's item: per-lane scale row
+  int gnb = 0;
+  auto issue_stage = [&]() {
     if (ls == 0) setup(li);
     const uint32_t base = lds0 + L::B + (issued % BL::NBS) * BL::STAGE;
     const int ks = k_stage(sc, load_nb, ls);
     const int bo = ks * (TBK * Fmt<WF>::BITS / 8);
 #pragma unroll
     for (int i = 0; i < BL::PER_WAVE; ++i) lds_copy16(bsrc[i] + bo, base + 1024 * (BL::PER_WAVE * bw + i));
-    lds_copy4(ssrc + 4 * ks, base + BL::CODES + 256 * bw);
     ++issued;
     if (++ls == sc.nk) {
       ls = 0;
       ++li;
     }
   };
-  for (int s = 0; s < BL::NBS - 1 && s < sc.total; ++s) issue_next();
+  // scale group G: 16 bytes (4 stages) of weight rows 64 bw + lane
+  auto issue_group = [&](int G) {
+    if (gls == 0) {
+      const ItemGeom it = item_geom<TM>(p, sc, gli);
+      gnb = it.nb;
+      gsrc = p.w_scale + (int64_t)it.expert * p.ws_estride + w_row<FC1>(p, it.nb, 64 * bw + lane) * (K / 32);
+    }
+    lds_copy16(gsrc + 4 * k_stage(sc, gnb, gls), lds0 + L::BS + (G & 1) * BL::GROUP + 1024 * bw);
+    gls += 4;
+    if (gls == sc.nk) {
+      gls = 0;
+      ++gli;
+    }
+  };
+  for (int G = 0; G < 2 && G < cnt.ngroups; ++G) issue_group(G);
+  for (int s = 0; s < BL::NBS - 1 && s < sc.total; ++s) issue_stage();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
-    // stage gidx has landed once at most the stages issued after it remain
-    wait_stages<b_copies<WF, TM>(), BL::NBS - 2>(issued - 1 - gidx);
+    wait_vm_range<0, kMaxWait>(min(cnt.allowed(gidx), kMaxWait));
     barrier();
-    if (issued < sc.total) issue_next();
+    if (gidx >= 4 && (gidx & 3) == 0 && (gidx >> 2) + 1 < cnt.ngroups) issue_group((gidx >> 2) + 1);
+    if (issued < sc.total) issue_stage();
   }
 }
 

@@ -136,8 +136,9 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static int wbits(mx_elem_t f) { return f == MX_E2M1 ? 4 : (f == MX_E3M2 ? 6 : 8); }
 
 // Routed GEMMs run tiled (LDS-staged, M-tiles of up to kTiledRows rows) when the
-// activations are MXFP8 and the local experts average at least this many rows;
-// otherwise the stream kernels (16-row tiles, weights straight from HBM) run.
+// activations are MXFP8, H and I are multiples of kTiledKMultiple and the
+// local experts average at least this many rows; otherwise the stream kernels
+// (16-row tiles, weights straight from HBM) run.
 constexpr int kTiledMinRowsPerExpert = 16;
 // ... in M-tiles of kTiledRowsLow rows while the local experts average at most
 // this many rows (nearly every expert then fits one such tile)
@@ -182,9 +183,10 @@ static FusedPlan plan(const moe_problem_t& p) {
   // mid kernels) need A*k < 2^32
   const bool kdiv_ok = (double)f.A * p.k < 4294967296.0;
   if (p.act == MOE_ACT_MXFP8) {
-    const bool tiled = f.L > 0 && f.A >= (int64_t)kTiledMinRowsPerExpert * f.L && p.H >= kTiledMinK &&
-                       p.I >= kTiledMinK;
-    const bool shared_tiled = p.T >= kTiledMinRowsPerExpert && p.H >= kTiledMinK && p.I_shared >= kTiledMinK;
+    const bool tiled_h = p.H % kTiledKMultiple == 0;
+    const bool tiled = f.L > 0 && f.A >= (int64_t)kTiledMinRowsPerExpert * f.L && tiled_h &&
+                       p.I % kTiledKMultiple == 0;
+    const bool shared_tiled = p.T >= kTiledMinRowsPerExpert && tiled_h && p.I_shared % kTiledKMultiple == 0;
     // E2M1 weights take the wide tiled kernel (256-row weight blocks)
     // (K a multiple of 512 and at least 1024: scale groups of 4 K-steps, items
     // of at least 8 steps)

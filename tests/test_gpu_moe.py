@@ -16,16 +16,17 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a
 CASES = {
     "tiny_w4a16": gen.WORKLOADS["tiny_w4a16"],
     "decode_w4a16_small": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=64, H=512, I=256, E=48),
-    "prefill_w4a8_small": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=300, H=512, I=384, E=16, k=4),
+    "prefill_w4a8_small": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=300, H=512, I=512, E=16, k=4),
     "skew_w4a16_small": gen.scaled(gen.WORKLOADS["skew_w4a16"], T=256, H=256, I=256, E=32, k=4),
-    "w6a8_shared_small": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=100, H=384, I=256, E=24, k=6,
+    "w6a8_shared_small": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=100, H=512, I=512, E=24, k=6,
                                     I_shared=512),
     "w6a8_no_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=33, H=256, I=128, E=8, k=3, I_shared=0),
     "w4a8_single_token": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=1, H=256, I=128, E=8, k=2),
-    # several 256-row M-tiles per expert with a ragged last tile
-    "w4a8_multi_tile": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=700, H=256, I=256, E=4, k=2),
-    "w6a8_multi_tile_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=300, H=384, I=256, E=2, k=2,
-                                         I_shared=256),
+    # several 192-row M-tiles per expert with a ragged last tile (the tiled
+    # kernel: K a multiple of 512 but below the wide kernel's 1024)
+    "w4a8_multi_tile": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=700, H=512, I=512, E=4, k=2),
+    "w6a8_multi_tile_shared": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=300, H=512, I=512, E=2, k=2,
+                                         I_shared=512),
     # enough (M-tile, N-block) items that every persistent workgroup of the
     # tiled GEMMs streams several of them back to back
     "w4a8_stream_items": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=512, H=2048, I=1024, E=32, k=4),
@@ -41,10 +42,10 @@ CASES = {
     "w4a8_wide_k1": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=400, H=1024, I=1024, E=4, k=1),
     # the tiled kernel with 128-row M-tiles (experts average at most 96 rows)
     # under skewed routing: some experts span several tiles, two get none
-    "w6a8_low_rows_skew": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=256, H=512, I=256, E=16, k=4,
+    "w6a8_low_rows_skew": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=256, H=512, I=512, E=16, k=4,
                                      I_shared=0, skew=True),
-    # MXFP8 activations x E2M1 with H not a multiple of 256: the 32x32 tiled
-    # kernel instead of the wide one
+    # MXFP8 activations with H not a multiple of 512: the 16-row stream kernels
+    # instead of the tiled or wide ones
     "w4a8_h384": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=200, H=384, I=256, E=4, k=2),
     # bf16 activations, experts averaging at least 32 rows: the 64-row mid-M
     # kernel; skewed routing gives experts of several M-tiles, ragged tails and
