@@ -41,4 +41,8 @@ hipError_t launch_permute(const int32_t* ids, const float* w, int T, int k, int 
                           int32_t* rank, int32_t* offsets, int32_t* sorted_assign, float* sorted_w, Tile* tiles,
                           int32_t* num_tiles, int bm, hipStream_t stream);
 
+// Batches of at most 64 tokens with T*k at most this many assignments take a
+// one-workgroup permutation (same results; hist and rank are not used).
+constexpr int kSmallRouteAssign = 4096;
+
 }  // namespace moe_mx

@@ -16,7 +16,8 @@
 //   2. one block scans the histograms over blocks (write bases) and over
 //      experts (expert offsets), and emits the GEMM tile list;
 //   3. every assignment is written to base + rank.
-// The order inside an expert segment is therefore ascending token.
+// The order inside an expert segment is therefore ascending token.  Batches of
+// at most 64 tokens (one token block) run the three steps in one workgroup.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -59,30 +60,25 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return m;
 }
 
-// 4 waves per block, one token per wave; E <= 1024 -> at most 16 logits per lane.
+// Top-k of one token by one wave; E <= 1024 -> at most 16 logits per lane.
 // Every lane sees the winner of each round, so all lanes carry the same
-// running softmax denominator; lane 0 writes ids and, in a second pass over
-// its own stores, the normalised weights.
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
-                                              int32_t* __restrict__ ids, float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wv;
-  if (t >= T) return;
-  const float* row = logits + (int64_t)t * E;
+// running softmax denominator.
+struct TopkToken {
   uint32_t key[16];
   uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? ordered_bits(row[e]) : 0u;
-  }
-  // lane j keeps the id and logit of slot j (k <= E <= 1024, so slots past
-  // 63 are kept by lane j % 64 in round j / 64)
   float top = 0.f, sum = 0.f;
-  for (int j0 = 0; j0 < k; j0 += 64) {
-    int my_e = 0;
-    float my_v = 0.f;
-    const int jn = min(k - j0, 64);
+
+  __device__ __forceinline__ TopkToken(const float* row, int E, int lane) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = lane + 64 * i;
+      key[i] = e < E ? ordered_bits(row[e]) : 0u;
+    }
+  }
+  // slots j0 .. j0+jn-1 (jn <= 64): lane jj gets slot j0+jj's expert and logit
+  __device__ __forceinline__ void select(int E, int j0, int jn, int lane, int& my_e, float& my_v) {
+    my_e = 0;
+    my_v = 0.f;
     for (int jj = 0; jj < jn; ++jj) {
       uint64_t best = 0;
 #pragma unroll
@@ -104,17 +100,34 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
         my_v = v;
       }
     }
+  }
+};
+
+// 4 waves per block, one token per wave.  Lane j keeps the id and logit of
+// slot j (k <= E <= 1024, so slots past 63 are kept by lane j % 64 in round
+// j / 64); lane j writes slot j's id and, once the sum is complete, weight.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  TopkToken tk(logits + (int64_t)t * E, E, lane);
+  for (int j0 = 0; j0 < k; j0 += 64) {
+    int my_e;
+    float my_v;
+    const int jn = min(k - j0, 64);
+    tk.select(E, j0, jn, lane, my_e, my_v);
     if (lane < jn) ids[(int64_t)t * k + j0 + lane] = my_e;
     if (k <= 64) {
       // one batch: the sum is complete, the slot's logit is still in a register
-      if (lane < jn) wts[(int64_t)t * k + lane] = expf(my_v - top) * (1.0f / sum);
+      if (lane < jn) wts[(int64_t)t * k + lane] = expf(my_v - tk.top) * (1.0f / tk.sum);
       return;
     }
     // the weights need the full sum: park the logits, normalised below
     if (lane < jn) wts[(int64_t)t * k + j0 + lane] = my_v;
   }
-  const float inv = 1.0f / sum;
-  for (int j = lane; j < k; j += 64) wts[(int64_t)t * k + j] = expf(wts[(int64_t)t * k + j] - top) * inv;
+  const float inv = 1.0f / tk.sum;
+  for (int j = lane; j < k; j += 64) wts[(int64_t)t * k + j] = expf(wts[(int64_t)t * k + j] - tk.top) * inv;
 }
 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
@@ -229,9 +242,82 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids
   if (sorted_w) sorted_w[pos] = w[a];
 }
 
+// Small batches (T <= 64 tokens, T*k <= kSmallRouteAssign): the three steps
+// of the permutation in one workgroup of 16 waves, with the same results: the
+// tokens are one token block, so an expert's mask of tokens gives its count
+// and, below a token, that token's rank.
+__global__ __launch_bounds__(1024) void k_permute_small(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                                                        int T, int k, int off, int L, int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ sorted_assign,
+                                                        float* __restrict__ sorted_w, Tile* __restrict__ tiles,
+                                                        int32_t* __restrict__ num_tiles, int bm) {
+  __shared__ unsigned long long mask[kMaxExperts];
+  __shared__ int32_t s_ids[kSmallRouteAssign];
+  __shared__ int32_t s_a[kMaxExperts];
+  __shared__ int32_t s_b[kMaxExperts];
+  __shared__ int32_t s_start[kMaxExperts];
+  const int e = threadIdx.x;  // one thread per local expert in the scan
+  const int A = T * k;
+  mask[e] = 0ull;
+  for (int a = e; a < A; a += 1024) s_ids[a] = ids[a];
+  __syncthreads();
+  for (int a = e; a < A; a += 1024) {
+    const int el = s_ids[a] - off;
+    if (el >= 0 && el < L) atomicOr(&mask[el], 1ull << (a / k));
+  }
+  __syncthreads();
+  // counts, inclusive scans of counts and tile counts over the experts,
+  // offsets and tiles (as k_scan with one token block)
+  const int32_t count = e < L ? __popcll(mask[e]) : 0;
+  const int32_t ntile = (e < L && bm > 0) ? (count + bm - 1) / bm : 0;
+  s_a[e] = count;
+  s_b[e] = ntile;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int32_t a = e >= d ? s_a[e - d] : 0;
+    const int32_t b = e >= d ? s_b[e - d] : 0;
+    __syncthreads();
+    s_a[e] += a;
+    s_b[e] += b;
+    __syncthreads();
+  }
+  const int32_t start = s_a[e] - count;
+  s_start[e] = start;
+  if (e < L) {
+    offsets[e] = start;
+    if (e == L - 1) offsets[L] = s_a[e];
+    const int32_t tstart = s_b[e] - ntile;
+    for (int i = 0; i < ntile; ++i) {
+      const int32_t r0 = i * bm;
+      Tile tl;
+      tl.expert = e;
+      tl.p0 = start + r0;
+      tl.rows = min(bm, count - r0);
+      tl.pad = 0;
+      tiles[tstart + i] = tl;
+    }
+  }
+  if (e == 0 && bm > 0) *num_tiles = s_b[1023];
+  __syncthreads();
+  for (int a = e; a < A; a += 1024) {
+    const int el = s_ids[a] - off;
+    if (el < 0 || el >= L) continue;
+    const int t = a / k;
+    const unsigned long long below = t ? (~0ull >> (64 - t)) : 0ull;
+    const int32_t pos = s_start[el] + __popcll(mask[el] & below);
+    sorted_assign[pos] = a;
+    if (sorted_w) sorted_w[pos] = w[a];
+  }
+}
+
 hipError_t launch_permute(const int32_t* ids, const float* w, int T, int k, int off, int L, int32_t* hist,
                           int32_t* rank, int32_t* offsets, int32_t* sorted_assign, float* sorted_w, Tile* tiles,
                           int32_t* num_tiles, int bm, hipStream_t stream) {
+  if (T <= 64 && (int64_t)T * k <= kSmallRouteAssign) {
+    k_permute_small<<<1, 1024, 0, stream>>>(ids, w, T, k, off, L, offsets, sorted_assign, sorted_w, tiles,
+                                            num_tiles, tiles ? bm : 0);
+    return hipGetLastError();
+  }
   const int nblk = (T + 63) / 64;
   if (nblk > 0) k_rank<<<nblk, 64, 0, stream>>>(ids, T, k, off, L, hist, rank);
   k_scan<<<1, 1024, 0, stream>>>(hist, nblk, L, offsets, tiles, num_tiles, tiles ? bm : 0);

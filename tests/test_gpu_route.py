@@ -38,7 +38,8 @@ def test_workload_logits(name):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (63, 384, 8), (65, 384, 8), (130, 17, 17), (7, 1024, 9),
-                                   (200, 1024, 1), (300, 64, 64), (9, 200, 100), (5, 1024, 130)])
+                                   (200, 1024, 1), (300, 64, 64), (9, 200, 100), (5, 1024, 130),
+                                   (64, 1024, 64), (64, 64, 1)])
 def test_ties_and_shapes(T, E, k):
     g = torch.Generator().manual_seed(T * 131 + E)
     logits = (torch.randint(-4, 5, (T, E), generator=g) * 0.5).float()   # many exact ties
