@@ -51,6 +51,7 @@
 #include "copy_ring.h"
 #include "gemm.h"
 #include "mx_device.h"
+#include "tiled_count.h"
 
 namespace moe_mx {
 
@@ -115,43 +116,6 @@ template <int WF, int TM> struct Lds {
   static constexpr int TBL = BS + 2 * BLay<WF, TM>::GROUP;
   static constexpr int TOTAL = TBL + ALay<TM>::TABLES * ALay<TM>::TABLE;
   static_assert(TOTAL <= 160 * 1024, "LDS");
-};
-
-// Memory-counter bookkeeping of a copy wave with an NS-stage ring, C copies
-// per stage and GC per scale group, in closed form.  Issue order: the prologue
-// copies scale groups 0 and 1, then stages 0 .. NS-2; after barrier x the wave
-// copies group x/4 + 1 when x % 4 == 0 and x >= 4 (into the buffer of group
-// x/4 - 1, whose last stage was read before barrier x), then stage x + NS - 1.
-// Stages and groups past the end of the stream are not issued and not
-// counted.  Row-table copies are left out: they only add copies in flight
-// after a given one, so leaving them out makes a wait stricter.  The copy
-// waves do nothing else, so the counts are computed at run time.
-template <int NS, int C, int GC>
-struct CopyCount {
-  int total, ngroups;
-  // copies issued through the slot after barrier x (x = -1: the prologue)
-  __device__ __forceinline__ int issued_through(int x) const {
-    return C * min(total, NS + x) + GC * min(ngroups, x >= 4 ? 2 + x / 4 : 2);
-  }
-  // copies issued up to and including stage s (issued in slot s - NS + 1,
-  // after that slot's group)
-  __device__ __forceinline__ int through_stage(int s) const {
-    const int x = s - NS + 1;
-    return C * (s + 1) + GC * min(ngroups, x >= 4 ? 2 + x / 4 : 2);
-  }
-  // copies issued up to and including group G (issued in slot 4G - 4, before
-  // that slot's stage; groups 0 and 1 open the prologue)
-  __device__ __forceinline__ int through_group(int G) const {
-    if (G < 2) return GC * (G + 1);
-    return C * min(total, NS + 4 * G - 5) + GC * (G + 1);
-  }
-  // copies that may stay in flight before barrier b: all but those up to
-  // stage b and, when b opens a group, that group
-  __device__ __forceinline__ int allowed(int b) const {
-    int need = through_stage(b);
-    if ((b & 3) == 0) need = max(need, through_group(b >> 2));
-    return issued_through(b - 1) - need;
-  }
 };
 
 // s_waitcnt vmcnt(n) lgkmcnt(0) for a run-time n in [LO, HI] (a compare ladder)
@@ -432,7 +396,7 @@ __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc
   const bool routed = p.dense_rows == 0;
   const uint32_t lds0 = lds_addr(smem);
   const int c = (lane & 7) ^ (lane >> 3);  // chunk that lands in this lane's LDS slot
-  const CopyCount<AL::STAGES, kACodeCopies, kGC> cnt{sc.total, sc.total / 4};
+  const TiledCopyCount<AL::STAGES, kACodeCopies, kGC> cnt{sc.total, sc.total / 4};
 
   // activation row (token for FC1, permuted row for FC2) of tile row r of
   // item li, whose row table must have landed
@@ -526,7 +490,7 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
   const int64_t wrow = (int64_t)K * Fmt<WF>::BITS / 8;
-  const CopyCount<BL::NBS, BL::PER_WAVE, 1> cnt{sc.total, sc.total / 4};
+  const TiledCopyCount<BL::NBS, BL::PER_WAVE, 1> cnt{sc.total, sc.total / 4};
 
   const uint8_t* bsrc[BL::PER_WAVE];
   int load_nb = 0;

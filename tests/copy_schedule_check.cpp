@@ -1,0 +1,64 @@
+// Host check of the tiled GEMM's closed-form copy counts (tiled_count.h): for
+// every ring shape the kernel instantiates, and stream lengths of 1 to 120
+// groups, replay the copy waves' issue sequence and compare, before every
+// barrier, the number of copies that may stay in flight with the exact count
+// (all copies issued so far after the last one the step needs).  Prints "ok"
+// and exits 0, or prints the first mismatch and exits 1.
+#include <cstdio>
+#include <vector>
+
+#include "tiled_count.h"
+
+struct Copy {
+  char kind;  // 'S' stage, 'G' scale group
+  int index;
+};
+
+template <int NS, int C, int GC>
+static bool check(int total) {
+  const int ngroups = total / 4;
+  std::vector<Copy> seq;
+  auto group = [&](int g) { for (int i = 0; i < GC; ++i) seq.push_back({'G', g}); };
+  auto stage = [&](int s) { for (int i = 0; i < C; ++i) seq.push_back({'S', s}); };
+  for (int g = 0; g < 2 && g < ngroups; ++g) group(g);
+  int issued = 0;
+  for (; issued < NS - 1 && issued < total; ++issued) stage(issued);
+  const moe_mx::TiledCopyCount<NS, C, GC> cnt{total, ngroups};
+  for (int b = 0; b < total; ++b) {
+    // exact: copies after the last copy of stage b and (at a group start) group b/4
+    int last = -1;
+    for (int i = 0; i < (int)seq.size(); ++i)
+      if ((seq[i].kind == 'S' && seq[i].index == b) || ((b & 3) == 0 && seq[i].kind == 'G' && seq[i].index == b / 4))
+        last = i;
+    if (last < 0) {
+      std::printf("NS=%d C=%d GC=%d total=%d: barrier %d needs a copy that was never issued\n", NS, C, GC, total, b);
+      return false;
+    }
+    const int exact = (int)seq.size() - 1 - last;
+    if (cnt.allowed(b) != exact) {
+      std::printf("NS=%d C=%d GC=%d total=%d barrier %d: closed form %d, replay %d\n", NS, C, GC, total, b,
+                  cnt.allowed(b), exact);
+      return false;
+    }
+    if (b >= 4 && (b & 3) == 0 && b / 4 + 1 < ngroups) group(b / 4 + 1);
+    if (issued < total) stage(issued++);
+  }
+  return true;
+}
+
+template <int NS, int C, int GC>
+static bool sweep() {
+  for (int groups = 1; groups <= 120; ++groups)
+    if (!check<NS, C, GC>(4 * groups)) return false;
+  return true;
+}
+
+int main() {
+  // activation waves: 4 stages, 8 or 12 code copies (128- or 192-row tiles),
+  // 1 or 2 group copies; weight waves: 6/4 (192-row tiles, E2M1/E3M2) or 10/7
+  // (128-row tiles) stages of 4 or 6 copies, 1 group copy
+  const bool ok = sweep<4, 8, 1>() && sweep<4, 12, 2>() && sweep<6, 4, 1>() && sweep<4, 6, 1>() &&
+                  sweep<10, 4, 1>() && sweep<7, 6, 1>();
+  std::printf(ok ? "ok\n" : "FAILED\n");
+  return ok ? 0 : 1;
+}
