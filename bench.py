@@ -53,7 +53,7 @@ FC1_KERNEL = {
 # while these are unchanged since it was taken.
 KERNEL_SOURCES = tuple(f"block_scaled_precision_amd/csrc/{f}" for f in (
     "copy_ring.h", "gemm.h", "gemm_mid.hip", "gemm_small.hip", "gemm_stream.hip", "gemm_tiled.hip", "gemm_wide.hip",
-    "internal.h", "mx_device.h", "tiled_count.h"))
+    "internal.h", "mx_device.h", "tiled_count.h", "wide_count.h"))
 
 
 def parse():

@@ -47,6 +47,7 @@
 #include "copy_ring.h"
 #include "gemm.h"
 #include "mx_device.h"
+#include "wide_count.h"
 
 namespace moe_mx {
 
@@ -80,7 +81,7 @@ static_assert(TBM == 192 && TBN == 256, "copy maps below assume 192 x 256 items"
 constexpr int kAStages = 3;
 constexpr int kBStages = 4;
 constexpr int kTables = 4;
-constexpr int kGroup = 4;  // K-steps per scale group
+constexpr int kGroup = kWideGroup;  // K-steps per scale group
 // The row table of item i+1 is copied when item i's first stage is copied,
 // kAStages steps before item i starts, into the buffer of item i+1-kTables,
 // whose last reader is its epilogue at the end of item i+2-kTables: with items
@@ -187,57 +188,25 @@ __device__ __forceinline__ void copy_table(const FcArgs& p, const ItemGeom& it, 
   }
 }
 
-// Memory-counter bookkeeping of a copy stream in closed form.  A wave issues
-// its prologue (code stages 0..NS-1, C copies each, then scale groups 0 and
-// 1, one copy each) and after barrier g the code stage of step g+NS and, when
-// g % 4 == 3, scale group (g+1)/4 + 1.  Row-table copies are left out of the
-// count: they only add to the copies in flight after a given one, so leaving
-// them out makes a wait stricter, never looser.  Stages or groups past the end
-// of the stream are not issued but are counted, which would make a wait
-// looser (copies complete in issue order, so a wait that assumes more younger
-// copies than exist can pass before the one it guards); the last waits of a
-// stream, from barrier total - kTailWaits on, therefore wait for every copy.
-// barriers at the end of a stream whose waits could count a skipped copy: a
-// code stage is skipped from barrier total - NS on (NS <= 4), a scale group
-// from barrier total - 5 on
-constexpr int kTailWaits = 5;
+// Memory-counter bookkeeping of a copy stream: WideCopyCount (wide_count.h)
+// gives, in closed form, how many copies may stay in flight before each
+// barrier; its per-phase steady values are never looser than the exact count
+// (checked here at compile time and, against a replay of the issue sequence,
+// by a host program in the tests).  The last waits of a stream, from barrier
+// total - kTailWaits on, wait for every copy.
+constexpr int kTailWaits = kWideTailWaits;
 static_assert(kTailWaits >= kAStages - 1 && kTailWaits >= kBStages - 1 && kGroup + 1 <= kTailWaits, "tail waits");
 
 template <int NS, int C>
-struct CopyCount {
-  static constexpr int P = NS * C + 2;
-  // copies issued before barrier g
-  static constexpr int before(int g) { return P + g * C + g / kGroup; }
-  // copies issued up to and including code stage s / scale group G
-  static constexpr int code_end(int s) {
-    return s < NS ? (s + 1) * C : P + (s - NS + 1) * C + (s - NS) / kGroup;
-  }
-  static constexpr int group_end(int G) {
-    return G < 2 ? NS * C + G + 1 : P + (kGroup * G - kGroup) * C + (G - 2) + 1;
-  }
-  // copies that may stay in flight before barrier g: all but those up to the
-  // code stage of step g+1 and, when step g+1 opens a scale group, that group
-  static constexpr int allowed(int g) {
-    const int ce = code_end(g + 1);
-    const int need = ((g + 1) % kGroup) == 0 ? (ce > group_end((g + 1) / kGroup) ? ce : group_end((g + 1) / kGroup)) : ce;
-    return before(g) - need;
-  }
-  // From step kGroup on, allowed(g) depends only on g % kGroup; over the first
-  // steps it is larger.  So the steady-state value of g's phase is never looser
-  // than the exact count, and each wait is a compile-time immediate.
-  static constexpr int steady(int q) { return allowed(4 * kGroup + q); }
-  static constexpr bool steady_is_safe() {
-    for (int g = 0; g < 8 * kGroup; ++g)
-      if (steady(g % kGroup) > allowed(g)) return false;
-    return true;
-  }
-  static_assert(kGroup == 4 && steady_is_safe(), "per-phase waits");
+struct CopyCount : WideCopyCount<NS, C> {
+  using W = WideCopyCount<NS, C>;
+  static_assert(kGroup == 4 && W::steady_is_safe(), "per-phase waits");
   static __device__ __forceinline__ void wait_step(int g) {
     switch (g & (kGroup - 1)) {
-      case 0: wait_vm_lgkm0<steady(0)>(); break;
-      case 1: wait_vm_lgkm0<steady(1)>(); break;
-      case 2: wait_vm_lgkm0<steady(2)>(); break;
-      default: wait_vm_lgkm0<steady(3)>(); break;
+      case 0: wait_vm_lgkm0<W::steady(0)>(); break;
+      case 1: wait_vm_lgkm0<W::steady(1)>(); break;
+      case 2: wait_vm_lgkm0<W::steady(2)>(); break;
+      default: wait_vm_lgkm0<W::steady(3)>(); break;
     }
   }
 };

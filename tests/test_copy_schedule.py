@@ -1,8 +1,8 @@
-"""The tiled GEMM's copy waves wait with counts computed in closed form from
-their fixed issue order (tiled_count.h); a count that is too large would let
-a barrier pass before its stage has landed, silently.  A host program replays
-the issue sequence for every ring shape the kernel instantiates and compares
-(no GPU needed)."""
+"""The tiled and wide GEMMs' copy waves wait with counts computed in closed
+form from their fixed issue order (tiled_count.h, wide_count.h); a count that
+is too large would let a barrier pass before its stage has landed, silently.
+A host program replays the issue sequences for every ring shape the kernels
+instantiate and compares (no GPU needed)."""
 import os
 import shutil
 import subprocess
@@ -16,7 +16,7 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="needs hipcc")
-def test_tiled_copy_counts_match_replay(tmp_path):
+def test_copy_counts_match_replay(tmp_path):
     exe = tmp_path / "copy_schedule_check"
     src = os.path.join(ROOT, "tests", "copy_schedule_check.cpp")
     subprocess.run([HIPCC, "-O1", "-x", "hip", "--offload-arch=gfx950", "-I", CSRC, src, "-o", str(exe)],
