@@ -123,32 +123,40 @@ def test_repeat_is_stable():
     assert d < 1e-2
 
 
-def test_precomputed_topk_matches_router():
-    w, gw, arrs, shared, x, logits, m = _prepare("decode_w4a16_small")
-    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act)
+@pytest.mark.parametrize("name", ["decode_w4a16_small", "prefill_w4a8_small", "w6a8_shared_small"])
+def test_precomputed_topk_matches_router(name):
+    w, gw, arrs, shared, x, logits, m = _prepare(name)
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared)
     ids, wts, _, _ = m.moe_route(logits.cuda(), w.k)
-    print_flush("moe_fused with precomputed top-k")
+    print_flush(f"moe_fused {name} with precomputed top-k")
     y = m.moe_fused(prob, x.cuda(), gw, topk_ids_in=ids, topk_w_in=wts).float().cpu().numpy()
     torch.cuda.synchronize()
     ref = _oracle_y(w, arrs, shared, x, None, topk_ids=ids.cpu().numpy(), topk_w=wts.cpu().numpy())
-    assert_y_close(y, ref["y"], "precomputed")
+    assert_y_close(y, ref["y"], f"precomputed {name}")
 
 
-def test_expert_shards_sum_to_full_layer():
-    w, gw, arrs, shared, x, logits, m = _prepare("decode_w4a16_small")
+# (case, experts per shard) over the small-M, tiled (with a shared expert)
+# and wide kernels; the shared expert, when there is one, is added by shard 0
+@pytest.mark.parametrize("name,L", [("decode_w4a16_small", 12), ("prefill_w4a8_small", 4),
+                                    ("w6a8_shared_small", 8), ("w4a8_wide_multi_tile", 2)])
+def test_expert_shards_sum_to_full_layer(name, L):
+    w, gw, arrs, shared, x, logits, m = _prepare(name)
     parts = []
-    L = 12
     for r in range(w.E // L):
         sl = slice(r * L, (r + 1) * L)
-        shard = m.MoeWeights(gw.w1[sl], gw.w1_scale[sl], gw.w2[sl], gw.w2_scale[sl], w.wfmt)
-        prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, local_offset=r * L, local_count=L)
-        print_flush(f"moe_fused shard {r}")
+        own_shared = r == 0 and w.I_shared > 0
+        extra = (gw.ws1, gw.ws1_scale, gw.ws2, gw.ws2_scale) if own_shared else ()
+        shard = m.MoeWeights(gw.w1[sl], gw.w1_scale[sl], gw.w2[sl], gw.w2_scale[sl], w.wfmt, *extra)
+        prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared if own_shared else 0,
+                              local_offset=r * L, local_count=L)
+        print_flush(f"moe_fused {name} shard {r}")
         yp = m.moe_fused(prob, x.cuda(), shard, router_logits=logits.cuda()).float().cpu().numpy()
-        refp = _oracle_y(w, arrs, shared, x, logits, local_offset=r * L, local_count=L)["y"]
-        assert_y_close(yp, refp, f"shard {r}")
+        refp = _oracle_y(w, arrs, shared if own_shared else None, x, logits, local_offset=r * L,
+                         local_count=L)["y"]
+        assert_y_close(yp, refp, f"{name} shard {r}")
         parts.append(yp.astype(np.float64))
     full = _oracle_y(w, arrs, shared, x, logits)["y"]
-    assert_y_close(sum(parts), full, "shard sum")
+    assert_y_close(sum(parts), full, f"{name} shard sum")
 
 
 def test_zero_tokens_is_noop():
