@@ -159,6 +159,21 @@ def test_expert_shards_sum_to_full_layer(name, L):
     assert_y_close(sum(parts), full, f"{name} shard sum")
 
 
+def test_shard_without_assignments_is_zero():
+    """A shard whose experts no token selects (the skewed router's two -inf
+    experts): empty tile lists for the tiled GEMMs, and y exactly zero."""
+    w, gw, arrs, shared, x, logits, m = _prepare("w6a8_low_rows_skew")
+    off, L = w.E - 2, 2
+    shard = m.MoeWeights(gw.w1[off:], gw.w1_scale[off:], gw.w2[off:], gw.w2_scale[off:], w.wfmt)
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, local_offset=off, local_count=L)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    print_flush("moe_fused shard of unselected experts")
+    y = m.moe_fused(prob, x.cuda(), shard, router_logits=logits.cuda(), topk_ids_out=ids)
+    torch.cuda.synchronize()
+    assert not np.isin(ids.cpu().numpy(), [off, off + 1]).any()
+    assert torch.count_nonzero(y).item() == 0
+
+
 def test_zero_tokens_is_noop():
     w, gw, arrs, shared, x, logits, m = _prepare("tiny_w4a16")
     prob = m.make_problem(0, w.H, w.I, w.E, w.k, w.wfmt, w.act)
