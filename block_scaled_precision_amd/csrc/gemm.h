@@ -50,16 +50,20 @@ constexpr int kStreamRows = 16;
 hipError_t launch_fc_stream(const FcArgs& p, bool fc1, bool mx_act, int wfmt, hipStream_t st);
 
 // Tiled variant (MXFP8 activations): M-tiles of up to `rows` rows (kTiledRows,
-// or kTiledRowsLow when experts see fewer rows: less LDS for activations, a
-// deeper weight ring), N-blocks of 64 h columns (FC1: nchunks = I / 64) or 128
-// output columns (FC2: nchunks = H / 128); `grid` persistent workgroups (rounded
-// down to a multiple of 8, at least 8).  Requires K to be a multiple of
-// kTiledKMultiple (scales travel in groups of 4 128-K stages).
+// or kTiledRowsLow when experts see fewer rows: less LDS for activations,
+// room for wider N-blocks), N-blocks of tiled_weight_rows(rows) weight rows,
+// i.e. half as many h columns (FC1: nchunks = I / (that / 2)) or that many
+// output columns (FC2: nchunks = H / that); `grid` persistent workgroups
+// (rounded down to a multiple of 8, at least 8).  Requires K to be a multiple
+// of kTiledKMultiple (scales travel in groups of 4 128-K stages).
 constexpr int kTiledRows = 192;
 constexpr int kTiledRowsLow = 128;
-constexpr int kTiledColsFc1 = 64;
-constexpr int kTiledColsFc2 = 128;
 constexpr int kTiledKMultiple = 512;
+// weight rows per N-block of the tiled kernel for M-tiles of `rows` rows
+constexpr int tiled_weight_rows(int rows) { return rows == kTiledRowsLow ? 256 : 128; }
+// N-blocks of the small-M kernel: 64 h columns (FC1) or 128 output columns (FC2)
+constexpr int kSmallColsFc1 = 64;
+constexpr int kSmallColsFc2 = 128;
 hipError_t launch_fc_tiled(const FcArgs& p, bool fc1, int wfmt, int rows, int grid, hipStream_t st);
 
 // Wide variant (MXFP8 activations x E2M1 weights): M-tiles of up to kTiledRows

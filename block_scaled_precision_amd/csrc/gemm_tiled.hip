@@ -7,9 +7,12 @@
 //
 // Work item = (M-tile, N-block).  An M-tile holds up to 192 permuted rows of one
 // expert, so an expert with <= 192 assignments streams its weights from HBM
-// exactly once (128 rows when the experts average at most 96: the activation
-// ring shrinks and the weight ring deepens); the N-block is 128 weight rows (FC1: 64 gate rows and the 64
-// matching up rows, i.e. 64 columns of h; FC2: 128 output columns).  The grid is
+// exactly once; the N-block is TN = 128 weight rows (FC1: 64 gate rows and the
+// 64 matching up rows, i.e. 64 columns of h; FC2: 128 output columns).  When
+// the experts average at most 96 rows the M-tile is 128 rows and the N-block
+// TN = 256 weight rows: the activation stages shrink by a third, so each
+// 128-K step (one barrier) can carry twice the weight bytes and twice the
+// multiply work of the few rows an expert has.  The grid is
 // persistent: one workgroup per CU walks the items of its XCD (whole M-tiles
 // x, x+8, ..., then an equal share of the N-blocks of the last ntiles % 8
 // tiles), so the N-blocks of one M-tile run together on one XCD and its
@@ -18,18 +21,20 @@
 // step.
 //
 // Waves have fixed roles (12 waves, three per SIMD):
-//  * waves 0-7 multiply: wave (wm, wn) = (w / 2, w % 2) owns the 32-row
-//    sub-blocks wm and wm + 4 of the tile (so a partly filled tile still
-//    spreads over all SIMDs) and two 32-column MFMA tiles, reads its operands
-//    from LDS and writes the item's results;
+//  * waves 0-7 multiply: with WN = TN / 64 waves along N and WM = 8 / WN
+//    along M, wave (wm, wn) = (w / WN, w % WN) owns the 32-row sub-blocks
+//    wm, wm + WM, ... of the tile (so a partly filled tile still spreads over
+//    all SIMDs) and two 32-column MFMA tiles (64 weight rows), reads its
+//    operands from LDS and writes the item's results;
 //  * waves 8-9 copy the activation stage (gathered rows of E4M3 codes, 128 B per
-//    row and stage) into a ring of 4 LDS buffers, three stages ahead of the
-//    multiply, and the rows' scale words in groups of 4 stages;
+//    row and stage) into a ring of 4 LDS buffers (3 for E3M2 weights with
+//    128-row tiles), all but one stage ahead of the multiply, and the rows'
+//    scale words in groups of 4 stages;
 //  * waves 10-11 copy the weight stage (64 B per row and stage for E2M1, 96 B
-//    for E3M2) into a deeper ring (with 192-row tiles 6 buffers for E2M1, 4
-//    for E3M2; with 128-row tiles 10 and 7) so that weights, which come from
-//    HBM, are requested further ahead, and the rows' scale words in groups of
-//    4 stages.
+//    for E3M2) into a ring that takes the rest of the LDS (with 192-row tiles
+//    6 buffers for E2M1, 4 for E3M2; with 128-row tiles and 256-row N-blocks
+//    5 and 4) so that weights, which come from HBM, are requested further
+//    ahead, and the rows' scale words in groups of 4 stages.
 // The copies are global_load_lds (global memory straight into LDS) issued from
 // inline assembly; each copy wave waits for its own stage with an explicit
 // vmcnt before the barrier.  Because a wave's memory counter drains in order,
@@ -59,7 +64,6 @@ namespace {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int TBN = 128;         // weight rows per work item
 constexpr int TBK = 128;         // K per stage
 #ifndef MOE_TILED_MUL_WAVES
 #define MOE_TILED_MUL_WAVES 8
@@ -69,10 +73,19 @@ constexpr int kWaves = kComputeWaves + 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveA = kComputeWaves;      // first activation-copy wave
 constexpr int kWaveB = kComputeWaves + 2;  // first weight-copy wave
-constexpr int kGroupsM = kComputeWaves / 2;  // multiply waves along M
+
+// Work item shape for M-tiles of TM rows: TN weight rows, and the grid of
+// multiply waves (each holds 64 weight rows: two 32-column MFMA tiles)
+template <int TM> struct Grid {
+  static constexpr int TN = tiled_weight_rows(TM);
+  static_assert(kComputeWaves == 8 || TN == 128, "4 multiply waves only with 128-row N-blocks");
+  static constexpr int WN = TN / 64;               // multiply waves along N
+  static constexpr int WM = kComputeWaves / WN;    // multiply waves along M
+  static constexpr int MAX_SUB = (TM / 32 + WM - 1) / WM;  // 32-row sub-blocks per multiply wave
+};
 
 // LDS layout: [A ring: STAGES x codes TM x 128 B] [B ring: NBS x weight codes]
-//             [A scale groups: 2 x TM x 16 B] [B scale groups: 2 x TBN x 16 B]
+//             [A scale groups: 2 x TM x 16 B] [B scale groups: 2 x TN x 16 B]
 //             [row tables: TABLES x (source row TM x 4 B + weight TM x 4 B)]
 // for M-tiles of TM rows (kTiledRows or kTiledRowsLow).  Scales travel in
 // groups of 4 stages: the 16 scale bytes of a row for 4 consecutive stages
@@ -80,16 +93,16 @@ constexpr int kGroupsM = kComputeWaves / 2;  // multiply waves along M
 // stages (a 4-byte copy per row and stage costs one memory request per row
 // for 4 bytes, as many requests as the codes themselves).  K is a multiple of
 // 512, so an item's steps fill whole groups.
-template <int TM> struct ALay {
+template <int WF, int TM> struct ALay {
   static_assert(TM % 64 == 0 && TM <= 256, "tile rows");
-  static constexpr int STAGES = 4;
+  // E3M2 stages of 256 weight rows (24 KB) leave room for 3 activation stages
+  static constexpr int STAGES = Grid<TM>::TN == 256 && WF == 2 ? 3 : 4;
   // The row table of item i+1 is copied with item i's first stage, STAGES - 1
   // steps before item i starts, into the buffer of item i+1-TABLES, whose last
   // reader is its epilogue at the end of item i+2-TABLES: with items of at
   // least 2 steps the copy comes after that epilogue.
   static constexpr int TABLES = 4;
   static_assert((TABLES - 2) * 2 >= STAGES, "row table ring too short");
-  static constexpr int MAX_SUB = (TM / 32 + kGroupsM - 1) / kGroupsM;  // 32-row sub-blocks per multiply wave
   static constexpr int CODE_COPIES = TM / 16;  // 1-KB code copies per activation-copy wave and stage
   static constexpr int SCALE_CHUNKS = TM / 64;  // 1-KB copies (64 rows x 16 B) in a scale group
   static constexpr int GROUP_COPIES = (SCALE_CHUNKS + 1) / 2;  // per activation-copy wave and group
@@ -97,24 +110,27 @@ template <int TM> struct ALay {
   static constexpr int GROUP = TM * 16;
   static constexpr int TABLE = TM * 8;
 };
-// The weight ring takes what the activation ring and the tables leave of the
-// LDS: with shorter M-tiles more weight stages (which come from HBM) are in
-// flight.
+// The weight ring takes what the activation ring, the scale groups and the
+// tables leave of the LDS (all of its 160 KB in every shape), so that as many
+// weight stages (which come from HBM) as fit are in flight.
 template <int WF, int TM> struct BLay {
+  static constexpr int TN = Grid<TM>::TN;
   static constexpr int ROW = WF == 1 ? 64 : 96;    // bytes of one weight row per stage
-  static constexpr int STAGE = TBN * ROW;
-  static constexpr int COPIES = STAGE / 1024;      // 1-KB copies per stage: 8 or 12
-  static constexpr int PER_WAVE = COPIES / 2;      // per weight-copy wave: 4 or 6
-  static constexpr int GROUP = TBN * 16;           // one 1-KB copy per weight-copy wave
-  static constexpr int NBS = TM == kTiledRows ? (WF == 1 ? 6 : 4) : (WF == 1 ? 10 : 7);  // ring depth
+  static constexpr int STAGE = TN * ROW;
+  static constexpr int COPIES = STAGE / 1024;      // 1-KB copies per stage: 8, 12, 16 or 24
+  static constexpr int PER_WAVE = COPIES / 2;      // per weight-copy wave
+  static constexpr int GROUP = TN * 16;
+  static constexpr int GROUP_COPIES = GROUP / 2048;  // 1-KB copies (64 rows) per weight-copy wave and group
+  static constexpr int NBS = TM == kTiledRows ? (WF == 1 ? 6 : 4) : (WF == 1 ? 5 : 4);  // ring depth
+  static_assert(COPIES % 2 == 0 && GROUP_COPIES * 2048 == GROUP, "copy split");
 };
 template <int WF, int TM> struct Lds {
   static constexpr int A = 0;
-  static constexpr int B = ALay<TM>::STAGES * ALay<TM>::STAGE;
+  static constexpr int B = ALay<WF, TM>::STAGES * ALay<WF, TM>::STAGE;
   static constexpr int AS = B + BLay<WF, TM>::NBS * BLay<WF, TM>::STAGE;
-  static constexpr int BS = AS + 2 * ALay<TM>::GROUP;
+  static constexpr int BS = AS + 2 * ALay<WF, TM>::GROUP;
   static constexpr int TBL = BS + 2 * BLay<WF, TM>::GROUP;
-  static constexpr int TOTAL = TBL + ALay<TM>::TABLES * ALay<TM>::TABLE;
+  static constexpr int TOTAL = TBL + ALay<WF, TM>::TABLES * ALay<WF, TM>::TABLE;
   static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
@@ -186,21 +202,21 @@ __device__ __forceinline__ int k_stage(const Sched& sc, int nb, int ls) {
   return s < sc.nk ? s : s - sc.nk;
 }
 
-// weight row held at B-tile row jr
-template <bool FC1>
+// weight row held at B-tile row jr of an N-block of TN rows
+template <bool FC1, int TN>
 __device__ __forceinline__ int64_t w_row(const FcArgs& p, int nb, int jr) {
-  if (FC1) return jr < TBN / 2 ? (int64_t)nb * (TBN / 2) + jr : (int64_t)p.N + nb * (TBN / 2) + jr - TBN / 2;
-  return (int64_t)nb * TBN + jr;
+  if (FC1) return jr < TN / 2 ? (int64_t)nb * (TN / 2) + jr : (int64_t)p.N + nb * (TN / 2) + jr - TN / 2;
+  return (int64_t)nb * TN + jr;
 }
 
 // ------------------------------------------------------------ multiply ---
 
-// One 128-K stage for a wave holding NM (1 to kMaxSub) sub-blocks: sub-block
-// wm + kGroupsM*m of the tile times the wave's two 32-column B tiles.  `ags`
+// One 128-K stage for a wave holding NM (1 to MAX_SUB) sub-blocks: sub-block
+// wm + WM*m of the tile times the wave's two 32-column B tiles.  `ags`
 // and `bgs` point at the stage's scale words in its scale group buffers (row
 // r's word at 16 r).
 template <int WF, int TM, int NM>
-__device__ __forceinline__ void compute_stage(v16f (&acc)[ALay<TM>::MAX_SUB][2], const uint8_t* as, const uint8_t* bs,
+__device__ __forceinline__ void compute_stage(v16f (&acc)[Grid<TM>::MAX_SUB][2], const uint8_t* as, const uint8_t* bs,
                                               const uint8_t* ags, const uint8_t* bgs, int wm, int brow0, int brow1) {
   using BL = BLay<WF, TM>;
   const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
@@ -234,7 +250,7 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[ALay<TM>::MAX_SUB][2],
   }
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    const int r = 32 * (wm + kGroupsM * m) + l32;
+    const int r = 32 * (wm + Grid<TM>::WM * m) + l32;
     asw[m] = *(const uint32_t*)(ags + 16 * r);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -265,17 +281,21 @@ template <bool FC1, int WF, int TM>
 __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
   using L = Lds<WF, TM>;
   using BL = BLay<WF, TM>;
-  using AL = ALay<TM>;
-  constexpr int kMaxSub = AL::MAX_SUB;
+  using AL = ALay<WF, TM>;
+  using G = Grid<TM>;
+  constexpr int kMaxSub = G::MAX_SUB;
+  constexpr int TN = G::TN;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  // 8 waves: (wm, wn) = (w / 2, w % 2), so the two multiply waves of a SIMD
-  // (w and w + 4) hold sub-blocks {wm, wm + 4} and {wm + 2, wm + 6};
+  // 8 waves: (wm, wn) = (w / WN, w % WN), so the two multiply waves of a SIMD
+  // (w and w + 4) hold different sub-blocks (TN = 128: {wm, wm + 4} and
+  // {wm + 2, wm + 6}) or different rows of the same N-block (TN = 256:
+  // sub-blocks {0, 2} and {1, 3}, so a 64-row tile keeps both busy);
   // 4 waves: (w % 2, w / 2)
-  const int wm = kComputeWaves == 8 ? wv >> 1 : wv & 1;
-  const int wn = kComputeWaves == 8 ? wv & 1 : wv >> 1;
+  const int wm = kComputeWaves == 8 ? wv / G::WN : wv & 1;
+  const int wn = kComputeWaves == 8 ? wv % G::WN : wv >> 1;
   const int l32 = lane & 31, g = lane >> 5;
   const int brow0 = FC1 ? 32 * wn : 64 * wn;
-  const int brow1 = FC1 ? TBN / 2 + 32 * wn : 64 * wn + 32;
+  const int brow1 = FC1 ? TN / 2 + 32 * wn : 64 * wn + 32;
 
   v16f acc[kMaxSub][2];
 #pragma unroll
@@ -286,7 +306,7 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
       for (int e = 0; e < 16; ++e) acc[m][n][e] = 0.f;
 
   // sub-blocks of this wave in a tile of `rows` rows
-  auto wave_subs = [&](int rows) { return max(0, (((rows + 31) >> 5) - wm + kGroupsM - 1) / kGroupsM); };
+  auto wave_subs = [&](int rows) { return max(0, (((rows + 31) >> 5) - wm + G::WM - 1) / G::WM); };
   int ci = 0, cs = 0;
   ItemGeom it = item_geom<TM>(p, sc, 0);
   int nm = wave_subs(it.rows);
@@ -313,7 +333,7 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
 #pragma unroll
     for (int m = 0; m < kMaxSub; ++m) {
       if (m >= nm) continue;
-      const int sbk = wm + kGroupsM * m;
+      const int sbk = wm + G::WM * m;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 32 * sbk + 8 * (i >> 2) + 4 * g + (i & 3);
@@ -327,7 +347,7 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
           const int sexp = block_exponent<3>(mx);
           if (row < it.rows) {
             const int64_t prow = it.p0 + row;
-            const int col0 = it.nb * (TBN / 2) + 32 * wn;
+            const int col0 = it.nb * (TN / 2) + 32 * wn;
             ((uint8_t*)p.out)[prow * p.N + col0 + l32] = (uint8_t)encode<3>(h * exp2_neg(sexp));
             if (l32 == 0) p.out_scale[prow * (p.N / 32) + col0 / 32] = (uint8_t)(sexp + 127);
           }
@@ -343,7 +363,7 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
             orow = tsrc[row];
             w = twt[row];
           }
-          uint16_t* o = p.obuf + orow * p.N + it.nb * TBN + 64 * wn + l32;
+          uint16_t* o = p.obuf + orow * p.N + it.nb * TN + 64 * wn + l32;
           o[0] = f32_to_bf16_rne(w * acc[m][0][i]);
           o[32] = f32_to_bf16_rne(w * acc[m][1][i]);
         }
@@ -386,7 +406,7 @@ __device__ __forceinline__ void copy_table(const FcArgs& p, const ItemGeom& it, 
 template <bool FC1, int WF, int TM>
 __device__ __forceinline__ void activation_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
   using L = Lds<WF, TM>;
-  using AL = ALay<TM>;
+  using AL = ALay<WF, TM>;
   constexpr int kACodeCopies = AL::CODE_COPIES;
   constexpr int kGC = AL::GROUP_COPIES;
   constexpr int kMaxWait = (AL::STAGES - 1) * kACodeCopies + 2 * kGC;
@@ -484,13 +504,15 @@ template <bool FC1, int WF, int TM>
 __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, uint8_t* smem) {
   using L = Lds<WF, TM>;
   using BL = BLay<WF, TM>;
-  constexpr int kMaxWait = (BL::NBS - 1) * BL::PER_WAVE + 2;
+  constexpr int TN = BL::TN;
+  constexpr int kGC = BL::GROUP_COPIES;
+  constexpr int kMaxWait = (BL::NBS - 1) * BL::PER_WAVE + 2 * kGC;
   static_assert(kMaxWait < 64, "vmcnt range");
   const int lane = threadIdx.x & 63, bw = (threadIdx.x >> 6) - kWaveB;
   const int K = p.K;
   const uint32_t lds0 = lds_addr(smem);
   const int64_t wrow = (int64_t)K * Fmt<WF>::BITS / 8;
-  const TiledCopyCount<BL::NBS, BL::PER_WAVE, 1> cnt{sc.total, sc.total / 4};
+  const TiledCopyCount<BL::NBS, BL::PER_WAVE, kGC> cnt{sc.total, sc.total / 4};
 
   const uint8_t* bsrc[BL::PER_WAVE];
   int load_nb = 0;
@@ -510,12 +532,12 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
         jr = cc / 6;
         ch = cc % 6;
       }
-      bsrc[i] = wb + w_row<FC1>(p, it.nb, jr) * wrow + 16 * ch;
+      bsrc[i] = wb + w_row<FC1, TN>(p, it.nb, jr) * wrow + 16 * ch;
     }
   };
   int li = 0, ls = 0, issued = 0;  // code cursor
   int gli = 0, gls = 0;            // group cursor
-  const uint8_t* gsrc = nullptr;   // the group cursor's item: per-lane scale row
+  const uint8_t* gsrc[kGC];        // the group cursor's item: per-lane scale rows
   int gnb = 0;
   auto issue_stage = [&]() {
     if (ls == 0) setup(li);
@@ -530,14 +552,20 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
       ++li;
     }
   };
-  // scale group G: 16 bytes (4 stages) of weight rows 64 bw + lane
+  // scale group G: 16 bytes (4 stages) of weight rows 64 (kGC bw + i) + lane
   auto issue_group = [&](int G) {
     if (gls == 0) {
       const ItemGeom it = item_geom<TM>(p, sc, gli);
       gnb = it.nb;
-      gsrc = p.w_scale + (int64_t)it.expert * p.ws_estride + w_row<FC1>(p, it.nb, 64 * bw + lane) * (K / 32);
+#pragma unroll
+      for (int i = 0; i < kGC; ++i)
+        gsrc[i] = p.w_scale + (int64_t)it.expert * p.ws_estride +
+                  w_row<FC1, TN>(p, it.nb, 64 * (kGC * bw + i) + lane) * (K / 32);
     }
-    lds_copy16(gsrc + 4 * k_stage(sc, gnb, gls), lds0 + L::BS + (G & 1) * BL::GROUP + 1024 * bw);
+    const int ks = k_stage(sc, gnb, gls);
+#pragma unroll
+    for (int i = 0; i < kGC; ++i)
+      lds_copy16(gsrc[i] + 4 * ks, lds0 + L::BS + (G & 1) * BL::GROUP + 1024 * (kGC * bw + i));
     gls += 4;
     if (gls == sc.nk) {
       gls = 0;

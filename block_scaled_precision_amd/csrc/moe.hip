@@ -152,13 +152,14 @@ constexpr int kMidHighMinRowsPerExpert = 96;
 // GEMM kernel family of one FC1/FC2 pair
 enum class Fc { kStream, kSmall, kMid, kTiled, kWide };
 
-// N-block width: FC1 in h columns, FC2 in output columns
-static int fc_cols(Fc k, bool fc1) {
+// N-block width: FC1 in h columns, FC2 in output columns (`rows`: the M-tile
+// height the kernel runs with)
+static int fc_cols(Fc k, bool fc1, int rows) {
   switch (k) {
     case Fc::kWide:
     case Fc::kMid: return fc1 ? kWideCols / 2 : kWideCols;
-    case Fc::kTiled:
-    case Fc::kSmall: return fc1 ? kTiledColsFc1 : kTiledColsFc2;
+    case Fc::kTiled: return fc1 ? tiled_weight_rows(rows) / 2 : tiled_weight_rows(rows);
+    case Fc::kSmall: return fc1 ? kSmallColsFc1 : kSmallColsFc2;
     default: return fc1 ? kStreamColsFc1 : kStreamColsFc2;
   }
 }
@@ -434,7 +435,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.ws_estride = 2 * (int64_t)I * (H / 32);
   a1.K = H;
   a1.N = I;
-  a1.nchunks = I / fc_cols(f.routed, true);
+  a1.nchunks = I / fc_cols(f.routed, true, f.bm);
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
   const int cus = device_cus();
@@ -461,7 +462,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a2.ws_estride = (int64_t)H * (I / 32);
   a2.K = I;
   a2.N = H;
-  a2.nchunks = H / fc_cols(f.routed, false);
+  a2.nchunks = H / fc_cols(f.routed, false, f.bm);
   a2.out = nullptr;
   a2.obuf = obuf;
   if (!ok(launch_fc(a2, false, f.routed))) return MOE_ERR_HIP;
@@ -476,7 +477,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s1.w_estride = 0;
     s1.ws_estride = 0;
     s1.N = Is;
-    s1.nchunks = Is / fc_cols(f.shared, true);
+    s1.nchunks = Is / fc_cols(f.shared, true, f.shared_bm);
     s1.out = ws + f.hs;
     s1.out_scale = (uint8_t*)(ws + f.hssc);
     if (!ok(launch_fc(s1, true, f.shared))) return MOE_ERR_HIP;
@@ -490,7 +491,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s2.w_estride = 0;
     s2.ws_estride = 0;
     s2.K = Is;
-    s2.nchunks = H / fc_cols(f.shared, false);
+    s2.nchunks = H / fc_cols(f.shared, false, f.shared_bm);
     s2.obuf = sbuf;
     (void)bytes_is;
     if (!ok(launch_fc(s2, false, f.shared))) return MOE_ERR_HIP;

@@ -98,12 +98,15 @@ static bool sweep_wide() {
 }
 
 int main() {
-  // activation waves: 4 stages, 8 or 12 code copies (128- or 192-row tiles),
-  // 1 or 2 group copies; weight waves: 6/4 (192-row tiles, E2M1/E3M2) or 10/7
-  // (128-row tiles) stages of 4 or 6 copies, 1 group copy
+  // activation waves: 4 stages (3 with E3M2 weights and 128-row tiles) of 8
+  // or 12 code copies (128- or 192-row tiles), 1 or 2 group copies; weight
+  // waves: 192-row tiles (128-row N-blocks) 6/4 stages (E2M1/E3M2) of 4 or 6
+  // copies and 1 group copy, 128-row tiles (256-row N-blocks) 5/4 stages of 8
+  // or 12 copies and 2 group copies
   // wide kernel: activation ring 3 stages of 6 copies, weight ring 4 of 4
-  const bool ok = sweep<4, 8, 1>() && sweep<4, 12, 2>() && sweep<6, 4, 1>() && sweep<4, 6, 1>() &&
-                  sweep<10, 4, 1>() && sweep<7, 6, 1>() && sweep_wide<3, 6>() && sweep_wide<4, 4>();
+  const bool ok = sweep<4, 8, 1>() && sweep<3, 8, 1>() && sweep<4, 12, 2>() && sweep<6, 4, 1>() &&
+                  sweep<4, 6, 1>() && sweep<5, 8, 2>() && sweep<4, 12, 2>() && sweep_wide<3, 6>() &&
+                  sweep_wide<4, 4>();
   std::printf(ok ? "ok\n" : "FAILED\n");
   return ok ? 0 : 1;
 }
