@@ -217,7 +217,10 @@ static FusedPlan plan(const moe_problem_t& p) {
   else if (f.routed == Fc::kMid)
     f.bm = f.A >= (int64_t)kMidHighMinRowsPerExpert * f.L ? kMidRowsHigh : kMidRows;
   else f.bm = kStreamRows;
-  f.shared_bm = f.shared == Fc::kMid ? (p.T >= kMidHighMinRowsPerExpert ? kMidRowsHigh : kMidRows) : kTiledRows;
+  // the dense shared expert on the tiled kernel: 128-row M-tiles with their
+  // 256-row N-blocks (more multiply work per barrier than 192 x 128)
+  if (f.shared == Fc::kMid) f.shared_bm = p.T >= kMidHighMinRowsPerExpert ? kMidRowsHigh : kMidRows;
+  else f.shared_bm = f.shared == Fc::kTiled ? kTiledRowsLow : kTiledRows;
   f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
   auto take = [&](size_t bytes) {
