@@ -46,7 +46,7 @@ FC1_KERNEL = {
     "decode_w4a16": "k_fc_small<true, 4>",
     "prefill_w4a8": "k_fc_wide<true>",
     "skew_w4a16": "k_fc_mid<true, 128>",
-    "w6a8_shared": "k_fc_tiled<true, 2, 128>",
+    "w6a8_shared": "k_fc_tiled<true, 2, 128, false>",
 }
 
 # Sources of the GEMM kernels: a committed HBM-traffic summary counts only

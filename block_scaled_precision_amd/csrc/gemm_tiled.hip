@@ -584,7 +584,10 @@ __device__ __forceinline__ void weight_role(const FcArgs& p, const Sched& sc, ui
 
 }  // namespace
 
-template <bool FC1, int WF, int TM>
+// DENSE: the launch is a dense expert (p.dense_rows > 0).  The code is the
+// same; the separate instantiation keeps the routed and dense launches apart
+// in kernel traces.
+template <bool FC1, int WF, int TM, bool DENSE>
 __global__ __launch_bounds__(kThreads, 1) void k_fc_tiled(FcArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Lds<WF, TM>::TOTAL];
   Sched sc;
@@ -609,8 +612,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_fc_tiled(FcArgs p) {
 
 template <bool FC1, int WF>
 static hipError_t launch_tiled_t(const FcArgs& p, int rows, int grid, hipStream_t st) {
-  if (rows == kTiledRowsLow) k_fc_tiled<FC1, WF, kTiledRowsLow><<<grid, kThreads, 0, st>>>(p);
-  else k_fc_tiled<FC1, WF, kTiledRows><<<grid, kThreads, 0, st>>>(p);
+  const bool dense = p.dense_rows > 0;
+  if (rows == kTiledRowsLow) {
+    if (dense) k_fc_tiled<FC1, WF, kTiledRowsLow, true><<<grid, kThreads, 0, st>>>(p);
+    else k_fc_tiled<FC1, WF, kTiledRowsLow, false><<<grid, kThreads, 0, st>>>(p);
+  } else {
+    if (dense) k_fc_tiled<FC1, WF, kTiledRows, true><<<grid, kThreads, 0, st>>>(p);
+    else k_fc_tiled<FC1, WF, kTiledRows, false><<<grid, kThreads, 0, st>>>(p);
+  }
   return hipGetLastError();
 }
 
