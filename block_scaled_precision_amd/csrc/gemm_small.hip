@@ -44,13 +44,10 @@ namespace moe_mx {
 
 namespace {
 
-#ifndef MOE_SMALL_BK
-#define MOE_SMALL_BK 256
-#endif
 constexpr int SBM = kStreamRows;  // 16 rows per M-tile
 constexpr int SBN = 128;          // weight rows per item
-constexpr int SBK = MOE_SMALL_BK; // K per stage (128 or 256)
-static_assert(SBK == kSmallK, "the host checks K divisibility against kSmallK");
+constexpr int SBK = kSmallK;      // K per stage (the host checks K divisibility against it)
+static_assert(SBK == 128 || SBK == 256, "stage K");
 constexpr int NSTAGE = SBK == 128 ? 12 : 6;  // ring depth (about 150 KB either way)
 constexpr int KPL = SBK / 4;      // k values per lane group and stage (one or two MX blocks)
 constexpr int BROW = SBK / 2;     // weight bytes per row and stage

@@ -65,10 +65,7 @@ namespace {
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int TBK = 128;         // K per stage
-#ifndef MOE_TILED_MUL_WAVES
-#define MOE_TILED_MUL_WAVES 8
-#endif
-constexpr int kComputeWaves = MOE_TILED_MUL_WAVES;  // 4 or 8 multiply waves
+constexpr int kComputeWaves = 8;  // multiply waves
 constexpr int kWaves = kComputeWaves + 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWaveA = kComputeWaves;      // first activation-copy wave
@@ -78,7 +75,6 @@ constexpr int kWaveB = kComputeWaves + 2;  // first weight-copy wave
 // multiply waves (each holds 64 weight rows: two 32-column MFMA tiles)
 template <int TM> struct Grid {
   static constexpr int TN = tiled_weight_rows(TM);
-  static_assert(kComputeWaves == 8 || TN == 128, "4 multiply waves only with 128-row N-blocks");
   static constexpr int WN = TN / 64;               // multiply waves along N
   static constexpr int WM = kComputeWaves / WN;    // multiply waves along M
   static constexpr int MAX_SUB = (TM / 32 + WM - 1) / WM;  // 32-row sub-blocks per multiply wave
@@ -286,13 +282,12 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
   constexpr int kMaxSub = G::MAX_SUB;
   constexpr int TN = G::TN;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  // 8 waves: (wm, wn) = (w / WN, w % WN), so the two multiply waves of a SIMD
-  // (w and w + 4) hold different sub-blocks (TN = 128: {wm, wm + 4} and
+  // (wm, wn) = (w / WN, w % WN), so the two multiply waves of a SIMD (w and
+  // w + 4) hold different sub-blocks (TN = 128: {wm, wm + 4} and
   // {wm + 2, wm + 6}) or different rows of the same N-block (TN = 256:
-  // sub-blocks {0, 2} and {1, 3}, so a 64-row tile keeps both busy);
-  // 4 waves: (w % 2, w / 2)
-  const int wm = kComputeWaves == 8 ? wv / G::WN : wv & 1;
-  const int wn = kComputeWaves == 8 ? wv % G::WN : wv >> 1;
+  // sub-blocks {0, 2} and {1, 3}, so a 64-row tile keeps both busy)
+  const int wm = wv / G::WN;
+  const int wn = wv % G::WN;
   const int l32 = lane & 31, g = lane >> 5;
   const int brow0 = FC1 ? 32 * wn : 64 * wn;
   const int brow1 = FC1 ? TN / 2 + 32 * wn : 64 * wn + 32;
