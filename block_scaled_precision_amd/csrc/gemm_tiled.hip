@@ -220,13 +220,18 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[Grid<TM>::MAX_SUB][2],
   uint32_t bsw[2];
   v8i av[2][NM];
   uint32_t asw[NM];
+  // scale words first, then the fragments of the first 64-K half, then the
+  // second: the first half's MFMAs wait only for the reads issued before them
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int jr = (n == 0 ? brow0 : brow1) + l32;
-    bsw[n] = *(const uint32_t*)(bgs + 16 * jr);
+  for (int n = 0; n < 2; ++n) bsw[n] = *(const uint32_t*)(bgs + 16 * ((n == 0 ? brow0 : brow1) + l32));
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int blk = 2 * kk + g;
+  for (int m = 0; m < NM; ++m) asw[m] = *(const uint32_t*)(ags + 16 * (32 * (wm + Grid<TM>::WM * m) + l32));
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const int blk = 2 * kk + g;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int jr = (n == 0 ? brow0 : brow1) + l32;
       if (WF == 1) {
         const uint4 v = *(const uint4*)(bs + b4_off(jr, blk));
         bv[kk][n] = (v8i){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
@@ -243,13 +248,9 @@ __device__ __forceinline__ void compute_stage(v16f (&acc)[Grid<TM>::MAX_SUB][2],
         }
       }
     }
-  }
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const int r = 32 * (wm + Grid<TM>::WM * m) + l32;
-    asw[m] = *(const uint32_t*)(ags + 16 * r);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int m = 0; m < NM; ++m) {
+      const int r = 32 * (wm + Grid<TM>::WM * m) + l32;
       const uint4 lo = *(const uint4*)(as + a_off(r, 4 * kk + g));
       const uint4 hi = *(const uint4*)(as + a_off(r, 4 * kk + 2 + g));
       av[kk][m] = (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
