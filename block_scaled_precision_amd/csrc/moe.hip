@@ -164,12 +164,32 @@ static int fc_cols(Fc k, bool fc1, int rows) {
   }
 }
 
+// M-tile height of a dense GEMM (the shared expert) on the tiled kernel: M
+// rows, N output columns (FC1: h columns), `grid` persistent workgroups.
+// 128-row tiles with 256-row N-blocks carry more multiply work per step;
+// 192-row tiles with 128-row N-blocks split the work more finely.  Take the
+// one whose busiest workgroup has the smaller area to multiply (ties: 128).
+static int dense_tiled_rows(int M, int N, bool fc1, int grid) {
+  int best = kTiledRowsLow;
+  int64_t best_cost = -1;
+  for (const int rows : {kTiledRowsLow, kTiledRows}) {
+    const int tn = tiled_weight_rows(rows);
+    const int64_t items = (int64_t)((M + rows - 1) / rows) * (N / (fc1 ? tn / 2 : tn));
+    const int64_t cost = (items + grid - 1) / grid * rows * tn;
+    if (best_cost < 0 || cost < best_cost) {
+      best = rows;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 struct FusedPlan {
   int L, off;
   int64_t A;
   Fc routed, shared;
   int bm;         // M-tile height of the routed tile list
-  int shared_bm;  // M-tile height of the shared expert (dense mode)
+  int shared_bm;  // M-tile height of the shared expert on the mid-M kernel
   int nblk, max_tiles;
   size_t ids, w, rank, hist, offsets, sorted, sorted_w, tiles, ntiles, xq, xs, h, hsc, hs, hssc, obuf, sbuf, total;
 };
@@ -217,10 +237,9 @@ static FusedPlan plan(const moe_problem_t& p) {
   else if (f.routed == Fc::kMid)
     f.bm = f.A >= (int64_t)kMidHighMinRowsPerExpert * f.L ? kMidRowsHigh : kMidRows;
   else f.bm = kStreamRows;
-  // the dense shared expert on the tiled kernel: 128-row M-tiles with their
-  // 256-row N-blocks (more multiply work per barrier than 192 x 128)
-  if (f.shared == Fc::kMid) f.shared_bm = p.T >= kMidHighMinRowsPerExpert ? kMidRowsHigh : kMidRows;
-  else f.shared_bm = f.shared == Fc::kTiled ? kTiledRowsLow : kTiledRows;
+  // (a dense shared expert on the tiled kernel picks its tile height per GEMM
+  // at launch, from the grid: dense_tiled_rows)
+  f.shared_bm = f.shared == Fc::kMid ? (p.T >= kMidHighMinRowsPerExpert ? kMidRowsHigh : kMidRows) : kTiledRows;
   f.max_tiles = (int)(f.A / f.bm + (f.A < f.L ? f.A : f.L));
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -442,9 +461,8 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.out = ws + f.h;
   a1.out_scale = (uint8_t*)(ws + f.hsc);
   const int cus = device_cus();
-  // M-tile height: the routed tile list's, or the shared expert's in dense mode
-  auto launch_fc = [&](const FcArgs& a, bool fc1, Fc kind) {
-    const int rows = a.dense_rows > 0 ? f.shared_bm : f.bm;
+  // rows: M-tile height (the routed tile list's, or the dense GEMM's)
+  auto launch_fc = [&](const FcArgs& a, bool fc1, Fc kind, int rows) {
     switch (kind) {
       case Fc::kSmall: return launch_fc_small(a, fc1, cus, stream);
       case Fc::kMid: return launch_fc_mid(a, fc1, rows, cus, stream);
@@ -453,7 +471,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
       default: return launch_fc_stream(a, fc1, mx, wf, stream);
     }
   };
-  if (!ok(launch_fc(a1, true, f.routed))) return MOE_ERR_HIP;
+  if (!ok(launch_fc(a1, true, f.routed, f.bm))) return MOE_ERR_HIP;
   // 6-7. FC2 + weighted combine into the fp32 accumulator
   if (!mark(MOE_STAGE_FC2)) return MOE_ERR_HIP;
   FcArgs a2 = a1;
@@ -468,11 +486,14 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a2.nchunks = H / fc_cols(f.routed, false, f.bm);
   a2.out = nullptr;
   a2.obuf = obuf;
-  if (!ok(launch_fc(a2, false, f.routed))) return MOE_ERR_HIP;
+  if (!ok(launch_fc(a2, false, f.routed, f.bm))) return MOE_ERR_HIP;
   // shared expert: a dense expert over all T tokens with its own weight
   if (!mark(MOE_STAGE_SHARED)) return MOE_ERR_HIP;
   if (Is > 0) {
-    const int64_t bytes_is = (int64_t)Is * wbits(p->w_fmt) / 8;
+    const bool st = f.shared == Fc::kTiled;
+    const int tgrid = cus < 8 ? 8 : cus & ~7;  // the tiled kernel's grid
+    const int rows1 = st ? dense_tiled_rows(T, Is, true, tgrid) : f.shared_bm;
+    const int rows2 = st ? dense_tiled_rows(T, H, false, tgrid) : f.shared_bm;
     FcArgs s1 = a1;
     s1.dense_rows = T;
     s1.w = t->ws1;
@@ -480,10 +501,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s1.w_estride = 0;
     s1.ws_estride = 0;
     s1.N = Is;
-    s1.nchunks = Is / fc_cols(f.shared, true, f.shared_bm);
+    s1.nchunks = Is / fc_cols(f.shared, true, rows1);
     s1.out = ws + f.hs;
     s1.out_scale = (uint8_t*)(ws + f.hssc);
-    if (!ok(launch_fc(s1, true, f.shared))) return MOE_ERR_HIP;
+    if (!ok(launch_fc(s1, true, f.shared, rows1))) return MOE_ERR_HIP;
     FcArgs s2 = a2;
     s2.dense_rows = T;
     s2.dense_weight = p->shared_weight;
@@ -494,10 +515,9 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     s2.w_estride = 0;
     s2.ws_estride = 0;
     s2.K = Is;
-    s2.nchunks = H / fc_cols(f.shared, false, f.shared_bm);
+    s2.nchunks = H / fc_cols(f.shared, false, rows2);
     s2.obuf = sbuf;
-    (void)bytes_is;
-    if (!ok(launch_fc(s2, false, f.shared))) return MOE_ERR_HIP;
+    if (!ok(launch_fc(s2, false, f.shared, rows2))) return MOE_ERR_HIP;
   }
   // 8. y = bf16(accumulator)
   if (!mark(MOE_STAGE_FINALIZE)) return MOE_ERR_HIP;

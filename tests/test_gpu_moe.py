@@ -40,6 +40,11 @@ CASES = {
                                    I_shared=1024, wfmt="e2m1"),
     # the wide kernel with one expert per token (token index = assignment id)
     "w4a8_wide_k1": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=400, H=1024, I=1024, E=4, k=1),
+    # a dense shared expert with more FC1 items than workgroups: on 256 CUs its
+    # FC1 takes 128-row tiles with 256-row N-blocks and its FC2 192-row tiles
+    # with 128-row N-blocks (smaller inputs take 192-row tiles for both)
+    "w6a8_shared_fc1_items": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=1024, H=512, I=512, E=8, k=2,
+                                        I_shared=4096),
     # the tiled kernel with 128-row M-tiles (experts average at most 96 rows)
     # under skewed routing: some experts span several tiles, two get none
     "w6a8_low_rows_skew": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=256, H=512, I=512, E=16, k=4,
