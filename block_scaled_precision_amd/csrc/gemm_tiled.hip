@@ -5,14 +5,15 @@
 // values, block-scaled MMA with FP32 accumulation; TokenSpeed SiTU page,
 // "Activation precision": MXFP8 activation x MXFP4 weight).
 //
-// Work item = (M-tile, N-block).  An M-tile holds up to 192 permuted rows of one
-// expert, so an expert with <= 192 assignments streams its weights from HBM
-// exactly once; the N-block is TN = 128 weight rows (FC1: 64 gate rows and the
-// 64 matching up rows, i.e. 64 columns of h; FC2: 128 output columns).  When
-// the experts average at most 96 rows the M-tile is 128 rows and the N-block
-// TN = 256 weight rows: the activation stages shrink by a third, so each
-// 128-K step (one barrier) can carry twice the weight bytes and twice the
-// multiply work of the few rows an expert has.  The grid is
+// Work item = (M-tile, N-block).  An M-tile holds up to TM permuted rows of one
+// expert (TM = 192 or 128, the host's choice: 128 when the experts average at
+// most 96 rows; for a dense expert, per GEMM), so an expert with <= TM
+// assignments streams its weights from HBM exactly once.  With TM = 192 the
+// N-block is TN = 128 weight rows (FC1: 64 gate rows and the 64 matching up
+// rows, i.e. 64 columns of h; FC2: 128 output columns); with TM = 128 it is
+// TN = 256: the activation stages are a third smaller, so each 128-K step (one
+// barrier) can carry twice the weight bytes and twice the multiply work of the
+// few rows an expert has.  The grid is
 // persistent: one workgroup per CU walks the items of its XCD (whole M-tiles
 // x, x+8, ..., then an equal share of the N-blocks of the last ntiles % 8
 // tiles), so the N-blocks of one M-tile run together on one XCD and its
