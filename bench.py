@@ -210,8 +210,8 @@ def cpu_baseline(torch, np, gen, w, seed, logits, x, y_gpu, ntok):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer has no "
-              "multi-GPU path in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library runs the "
+              "layer on one GPU, an expert shard per call, and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
