@@ -63,14 +63,15 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // Top-k of one token by one wave; E <= 1024 -> at most 16 logits per lane.
 // Every lane sees the winner of each round, so all lanes carry the same
 // running softmax denominator.
+template <int NS>  // key slots per lane: experts lane, lane + 64, ..., NS*64 >= E
 struct TopkToken {
-  uint32_t key[16];
+  uint32_t key[NS];
   uint32_t taken = 0;
   float top = 0.f, sum = 0.f;
 
   __device__ __forceinline__ TopkToken(const float* row, int E, int lane) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NS; ++i) {
       const int e = lane + 64 * i;
       key[i] = e < E ? ordered_bits(row[e]) : 0u;
     }
@@ -82,7 +83,7 @@ struct TopkToken {
     for (int jj = 0; jj < jn; ++jj) {
       uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < NS; ++i) {
         const int e = lane + 64 * i;
         if (e < E && !(taken >> i & 1u)) {
           const uint64_t kk = ((uint64_t)key[i] << 32) | (uint32_t)(kMaxExperts - 1 - e);
@@ -106,12 +107,13 @@ struct TopkToken {
 // 4 waves per block, one token per wave.  Lane j keeps the id and logit of
 // slot j (k <= E <= 1024, so slots past 63 are kept by lane j % 64 in round
 // j / 64); lane j writes slot j's id and, once the sum is complete, weight.
+template <int NS>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ wts) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
-  TopkToken tk(logits + (int64_t)t * E, E, lane);
+  TopkToken<NS> tk(logits + (int64_t)t * E, E, lane);
   for (int j0 = 0; j0 < k; j0 += 64) {
     int my_e;
     float my_v;
@@ -133,7 +135,14 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                        hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  k_topk<<<(T + 3) / 4, 256, 0, stream>>>(logits, T, E, k, ids, w);
+  // as many key slots per lane as E needs (the selection rounds walk them all)
+  const int g = (T + 3) / 4, ns = (E + 63) / 64;
+  if (ns <= 1) k_topk<1><<<g, 256, 0, stream>>>(logits, T, E, k, ids, w);
+  else if (ns <= 2) k_topk<2><<<g, 256, 0, stream>>>(logits, T, E, k, ids, w);
+  else if (ns <= 4) k_topk<4><<<g, 256, 0, stream>>>(logits, T, E, k, ids, w);
+  else if (ns <= 6) k_topk<6><<<g, 256, 0, stream>>>(logits, T, E, k, ids, w);
+  else if (ns <= 8) k_topk<8><<<g, 256, 0, stream>>>(logits, T, E, k, ids, w);
+  else k_topk<16><<<g, 256, 0, stream>>>(logits, T, E, k, ids, w);
   return hipGetLastError();
 }
 
@@ -170,10 +179,10 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   __shared__ int32_t s_a[kMaxExperts];
   __shared__ int32_t s_b[kMaxExperts];
   const int e = threadIdx.x;
-  // exclusive prefix of expert e's counts over the token blocks, 16 blocks
+  // exclusive prefix of expert e's counts over the token blocks, 32 blocks
   // per batch: all loads of a batch go out before its stores, so the walk
-  // costs one memory latency per 16 blocks instead of one per block
-  constexpr int kBatch = 16;
+  // costs one memory latency per 32 blocks instead of one per block
+  constexpr int kBatch = 32;
   int32_t count = 0;
   if (e < L) {
     for (int b0 = 0; b0 < nblk; b0 += kBatch) {
