@@ -13,9 +13,10 @@
 //   1. per block of 64 tokens, an LDS bit mask per expert marks which lanes
 //      (tokens) chose it; popcount gives the block histogram, and the popcount
 //      below a lane gives the rank of its assignment inside the block;
-//   2. one block scans the histograms over blocks (write bases) and over
-//      experts (expert offsets), and emits the GEMM tile list;
-//   3. every assignment is written to base + rank.
+//   2. one block scans the histograms over blocks (each block's base within
+//      its expert) and over experts (expert offsets), and emits the GEMM tile
+//      list;
+//   3. every assignment is written to expert offset + base + rank.
 // The order inside an expert segment is therefore ascending token.  Batches of
 // at most 64 tokens (one token block) run the three steps in one workgroup.
 #include <hip/hip_runtime.h>
@@ -212,16 +213,9 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
   const int32_t start = s_a[e] - (e < L ? count : 0);
   const int32_t tstart = s_b[e] - ntile;
   if (e < L) {
+    // hist keeps the prefix within the expert; the scatter adds offsets[e]
     offsets[e] = start;
     if (e == L - 1) offsets[L] = s_a[e];
-    for (int b0 = 0; b0 < nblk; b0 += kBatch) {
-      int32_t h[kBatch];
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i) h[i] = b0 + i < nblk ? hist[(int64_t)(b0 + i) * L + e] : 0;
-#pragma unroll
-      for (int i = 0; i < kBatch; ++i)
-        if (b0 + i < nblk) hist[(int64_t)(b0 + i) * L + e] = h[i] + start;
-    }
     for (int i = 0; i < ntile; ++i) {
       const int32_t r0 = i * bm;
       Tile tl;
@@ -239,14 +233,14 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
 // weight of the assignment, so that consumers of permuted rows read it directly)
 __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids, const float* __restrict__ w,
                                                  int T, int k, int off, int L, const int32_t* __restrict__ base,
-                                                 const int32_t* __restrict__ rank,
+                                                 const int32_t* __restrict__ offsets, const int32_t* __restrict__ rank,
                                                  int32_t* __restrict__ sorted_assign, float* __restrict__ sorted_w) {
   const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (a >= (int64_t)T * k) return;
   const int e = ids[a] - off;
   if (e < 0 || e >= L) return;
   const int64_t blk = (a / k) / 64;
-  const int32_t pos = base[blk * L + e] + rank[a];
+  const int32_t pos = offsets[e] + base[blk * L + e] + rank[a];
   sorted_assign[pos] = (int32_t)a;
   if (sorted_w) sorted_w[pos] = w[a];
 }
@@ -331,8 +325,8 @@ hipError_t launch_permute(const int32_t* ids, const float* w, int T, int k, int 
   if (nblk > 0) k_rank<<<nblk, 64, 0, stream>>>(ids, T, k, off, L, hist, rank);
   k_scan<<<1, 1024, 0, stream>>>(hist, nblk, L, offsets, tiles, num_tiles, tiles ? bm : 0);
   const int64_t A = (int64_t)T * k;
-  if (A > 0) k_scatter<<<(A + 255) / 256, 256, 0, stream>>>(ids, w, T, k, off, L, hist, rank, sorted_assign,
-                                                            sorted_w);
+  if (A > 0) k_scatter<<<(A + 255) / 256, 256, 0, stream>>>(ids, w, T, k, off, L, hist, offsets, rank,
+                                                            sorted_assign, sorted_w);
   return hipGetLastError();
 }
 
