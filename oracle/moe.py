@@ -80,20 +80,25 @@ def intermediate(h: np.ndarray, act: str) -> np.ndarray:
     raise ValueError(act)
 
 
-def expert_ffn(a: np.ndarray, w1: np.ndarray, w2: np.ndarray, act: str) -> np.ndarray:
-    """a [M, H] float64, decoded w1 [2I, H], decoded w2 [H, I] -> o [M, H]."""
+def expert_hidden(a: np.ndarray, w1: np.ndarray) -> np.ndarray:
+    """a [M, H] float64, decoded w1 [2I, H] -> h = SiLU(gate) * up [M, I] (FC1
+    and the gated activation, before the intermediate rounding)."""
     I = w1.shape[0] // 2
     z = a @ w1.T                      # FC1, K = H
     g, u = z[:, :I], z[:, I:]
-    h = silu(g) * u
-    ht = intermediate(h, act)
+    return silu(g) * u
+
+
+def expert_ffn(a: np.ndarray, w1: np.ndarray, w2: np.ndarray, act: str) -> np.ndarray:
+    """a [M, H] float64, decoded w1 [2I, H], decoded w2 [H, I] -> o [M, H]."""
+    ht = intermediate(expert_hidden(a, w1), act)
     return ht @ w2.T                  # FC2, K = I
 
 
 def moe_forward(x, logits, w1, w1_scale, w2, w2_scale, *, k, wfmt, act,
                 topk_ids=None, topk_w=None,
                 shared=None, shared_weight=1.0,
-                local_offset=0, local_count=None, tokens=None):
+                local_offset=0, local_count=None, tokens=None, intermediates=False):
     """Full layer output in float64.
 
     x [T, H] exact bf16 values (float64); logits [T, E] float32 (or None when
@@ -105,7 +110,10 @@ def moe_forward(x, logits, w1, w1_scale, w2, w2_scale, *, k, wfmt, act,
     per listed token.
 
     Returns dict(y, ids, w, counts, offsets, sorted_assign) where the routing
-    entries cover the computed tokens.
+    entries cover the computed tokens.  With ``intermediates`` it also holds
+    "intermediates": assignment id t*k + j (t indexing the computed tokens) ->
+    the FC2 input of that assignment: (E4M3 codes [I], E8M0 scales [I/32]) for
+    MXFP8 activations, or the bf16-rounded values [I] (float64) for bf16.
     """
     if wfmt not in _WFMT:
         raise ValueError(wfmt)
@@ -126,6 +134,7 @@ def moe_forward(x, logits, w1, w1_scale, w2, w2_scale, *, k, wfmt, act,
 
     a = activations(x[rows], act)
     y = np.zeros((rows.size, H), dtype=np.float64)
+    inter = {}
     for i in range(local_count):
         seg = sorted_assign[offsets[i]:offsets[i + 1]]
         if seg.size == 0:
@@ -134,6 +143,15 @@ def moe_forward(x, logits, w1, w1_scale, w2, w2_scale, *, k, wfmt, act,
         t_loc, slot = seg // k, seg % k
         d1 = decode_weight(w1[e], w1_scale[e], wfmt, H)
         d2 = decode_weight(w2[e], w2_scale[e], wfmt, I)
+        if intermediates:
+            h = expert_hidden(a[t_loc], d1)
+            if act == "mxfp8":
+                codes, scales = mx.quantize(h, "e4m3")
+                for r, asg in enumerate(seg):
+                    inter[int(asg)] = (codes[r], scales[r])
+            else:
+                for r, asg in enumerate(seg):
+                    inter[int(asg)] = intermediate(h[r:r + 1], act)[0]
         o = expert_ffn(a[t_loc], d1, d2, act)
         y[t_loc] += w[t_loc, slot][:, None] * o   # a token meets an expert at most once
     if shared is not None:
@@ -142,4 +160,7 @@ def moe_forward(x, logits, w1, w1_scale, w2, w2_scale, *, k, wfmt, act,
         d1 = decode_weight(ws1, ws1_scale, wfmt, H)
         d2 = decode_weight(ws2, ws2_scale, wfmt, Is)
         y += shared_weight * expert_ffn(a, d1, d2, act)
-    return dict(y=y, ids=ids, w=w, counts=counts, offsets=offsets, sorted_assign=sorted_assign)
+    out = dict(y=y, ids=ids, w=w, counts=counts, offsets=offsets, sorted_assign=sorted_assign)
+    if intermediates:
+        out["intermediates"] = inter
+    return out

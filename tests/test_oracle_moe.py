@@ -147,6 +147,64 @@ def test_shared_expert_adds_dense_mlp():
     assert np.allclose(both - base, dense, rtol=1e-10, atol=1e-13)
 
 
+@pytest.mark.parametrize("sw", [0.375, -2.0, 0.0])
+def test_shared_weight_scales_the_shared_expert(sw):
+    """The shared expert enters y as shared_weight * dense MLP: the difference
+    from the routed-only layer is that multiple of the textbook MLP (exact for
+    a power-of-two weight, since scaling by 2**n commutes with every rounding
+    after FC2), and weight 0 leaves the routed output unchanged."""
+    rng = np.random.default_rng(8)
+    p1, s1, p2, s2 = _weights(rng, E, I, H, "e2m1")
+    q1, r1, q2, r2 = _weights(rng, 1, I, H, "e2m1")
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    shared = (q1[0], r1[0], q2[0], r2[0])
+    base = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16")["y"]
+    got = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16", shared=shared,
+                         shared_weight=sw)["y"]
+    dense = _dense_mlp(x, om.decode_weight(q1[0], r1[0], "e2m1", H),
+                       om.decode_weight(q2[0], r2[0], "e2m1", I), "bf16")
+    assert np.allclose(got - base, sw * dense, rtol=1e-10, atol=1e-13)
+    if sw == 0.0:
+        assert np.array_equal(got, base)
+    else:
+        # the shared term is a nonzero multiple of the dense MLP, with sw's sign
+        one = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act="bf16", shared=shared)["y"]
+        assert np.allclose(got - base, sw * (one - base), rtol=1e-10, atol=1e-13)
+        assert np.abs(dense).max() > 0
+
+
+def test_intermediates_match_the_dataflow():
+    """The optional intermediates are the FC2 inputs of each assignment: E4M3
+    codes + E8M0 scales of SiLU(gate)*up per 32 along I (MXFP8), or its bf16
+    values; feeding them through decoded W2 reproduces the expert outputs."""
+    rng = np.random.default_rng(9)
+    p1, s1, p2, s2 = _weights(rng, E, I, H, "e2m1")
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    for act in ("mxfp8", "bf16"):
+        out = om.moe_forward(x, lg, p1, s1, p2, s2, k=2, wfmt="e2m1", act=act, intermediates=True)
+        inter = out["intermediates"]
+        assert sorted(inter) == list(range(T * 2))
+        y = np.zeros_like(out["y"])
+        for a, v in inter.items():
+            t, j = divmod(a, 2)
+            e = int(out["ids"][t, j])
+            if act == "mxfp8":
+                codes, scales = v
+                assert codes.dtype == np.uint8 and codes.shape == (I,) and scales.shape == (I // 32,)
+                h = mx.dequantize(codes, scales, "e4m3")
+            else:
+                h = v
+                assert np.array_equal(h, mx.round_to_bf16(h))
+            d2 = om.decode_weight(p2[e], s2[e], "e2m1", I)
+            d1 = om.decode_weight(p1[e], s1[e], "e2m1", H)
+            ref_h = _dense_mlp(_act_input(x[t:t + 1], act), d1, np.eye(I), act)[0]
+            assert np.array_equal(h, ref_h)
+            y[t] += out["w"][t, j] * (h @ d2.T)
+        assert np.allclose(y, out["y"], rtol=1e-12, atol=1e-15)
+
+
 def test_token_subset_and_precomputed_topk():
     rng = np.random.default_rng(6)
     p1, s1, p2, s2 = _weights(rng, E, I, H, "e2m1")
