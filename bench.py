@@ -1,17 +1,22 @@
 """Throughput of the fused MX mixture-of-experts layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
 
 One step is one moe_fused call over one batch: top-k routing of the router
 logits, permutation by expert, (MXFP8 quantization of x), FC1 + SiLU(gate)*up,
 FC2 + routing-weighted combine (+ shared expert) and the bf16 output.  Inputs
 and packed weights are synthetic, seeded and resident in HBM before the timed
-region starts.  Prints one JSON line with whole-layer tokens/s, the roofline of
-the dominant kernel (timed with HIP events on the library's stream), and the
-CPU oracle timed on a bounded sample of the same workload.
+region starts.
 
-Default workload: decode_w4a16 (T=64, H=7168, I=2048, E=384 resident MXFP4
-experts, top-8, bf16 activations).
+By default every workload is timed in this one process (the decode and
+prefill workloads share one weight set): W untimed warm-up steps, then K
+steps, each bracketed by HIP events on the layer's stream; a workload's time
+per step is the median over its K steps.  The printed JSON line is headed by
+the decode workload (T=64, H=7168, I=2048, E=384 resident MXFP4 experts,
+top-8, bf16 activations); "workloads" holds every workload's line, each with
+the roofline of its dominant kernel (FC1, timed with HIP events on the
+library's stream in a second pass of K steps).  The CPU oracle is timed on a
+bounded sample of the decode workload.
 """
 from __future__ import annotations
 
@@ -19,6 +24,8 @@ import argparse
 import hashlib
 import json
 import os
+import platform
+import statistics
 import sys
 import time
 
@@ -29,6 +36,9 @@ if ROOT not in sys.path:
 # Published MI355X peaks (dense, no sparsity).
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp6": 10100.0, "fp4": 10100.0}
+
+HEADLINE = "decode_w4a16"
+ORDER = ("tiny_w4a16", "decode_w4a16", "prefill_w4a8", "skew_w4a16", "w6a8_shared")
 
 # Which roof bounds each workload's dominant kernel (FC1), and the MFMA rate it
 # issues at: MXFP8 x MXFP4/MXFP6 scaled MFMAs run at the FP8 rate, bf16
@@ -59,16 +69,20 @@ KERNEL_SOURCES = tuple(f"block_scaled_precision_amd/csrc/{f}" for f in (
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_w4a16")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="all", help="one workload name, or 'all' (default)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=None,
-                    help="tokens of the workload the CPU oracle runs on (default: per workload)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16,
+                    help="tokens of the decode workload the CPU oracle runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM counters)")
     return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -111,13 +125,11 @@ def copy_calibration(torch):
                       "launches": 5}), flush=True)
 
 
-def build_inputs(torch, m, gen, w, seed):
-    """Logits, x and all packed weights on the GPU (fp32 weights drawn on the
-    GPU per expert and quantized by mx_quantize into place)."""
+def build_weights(torch, m, gen, w, seed):
+    """All packed weights of a workload on the GPU: fp32 weights drawn on the
+    GPU per expert and quantized by mx_quantize into place."""
     dev = "cuda"
     bits = m.FORMAT_BITS[w.wfmt]
-    logits = gen.router_logits(w, seed, device=dev)
-    x = gen.hidden_states(w, seed, device=dev)
     w1 = torch.empty((w.E, 2 * w.I, w.H * bits // 8), dtype=torch.uint8, device=dev)
     s1 = torch.empty((w.E, 2 * w.I, w.H // 32), dtype=torch.uint8, device=dev)
     w2 = torch.empty((w.E, w.H, w.I * bits // 8), dtype=torch.uint8, device=dev)
@@ -130,7 +142,7 @@ def build_inputs(torch, m, gen, w, seed):
         mw.ws1, mw.ws1_scale = m.mx_quantize(gen.shared_w1(w, seed, device=dev), w.wfmt)
         mw.ws2, mw.ws2_scale = m.mx_quantize(gen.shared_w2(w, seed, device=dev), w.wfmt)
     torch.cuda.synchronize()
-    return logits, x, mw
+    return mw
 
 
 def algorithmic_work(w, counts):
@@ -160,50 +172,144 @@ def algorithmic_work(w, counts):
                 layer_bytes=layer_bytes, layer_flops=flops, fc1_bytes=fc1_bytes, fc1_flops=fc1_flops)
 
 
-def cpu_baseline(torch, np, gen, w, seed, logits, x, y_gpu, ntok):
-    """Time the CPU oracle on the first `ntok` tokens of the workload and compare
-    its output with the GPU's rows for the same tokens."""
-    from oracle import moe as om
-    from tests.helpers import ExpertArrays, y_error
-    import concurrent.futures as cf
-    import multiprocessing as mp
+def time_workload(torch, np, m, gen, w, mw, args):
+    """Warm up, then K steps each bracketed by HIP events; a second pass of K
+    steps records the per-stage events.  Returns the workload's line."""
+    seed = args.seed
+    logits = gen.router_logits(w, seed, device="cuda")
+    x = gen.hidden_states(w, seed, device="cuda")
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared)
+    ws = torch.empty((max(m.moe_fused_workspace_bytes(prob), 1),), dtype=torch.uint8, device="cuda")
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
 
-    rows = np.arange(ntok)
-    lg = logits[:ntok].cpu().numpy()
+    def step(events=None):
+        m.moe_fused(prob, x, mw, router_logits=logits, y=y, workspace=ws, topk_ids_out=ids,
+                    topk_w_out=wts, stream=stream, stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = m.HipEvents(K + 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(0, stream)
+    for i in range(K):
+        step()
+        ev.record(i + 1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = [ev.elapsed_ms(i, i + 1) for i in range(K)]
+    ms_med = statistics.median(per_step)
+    ms_mean = ev.elapsed_ms(0, K) / K
+    # stage breakdown (events at every stage boundary cost a few us per step)
+    ns = m.MOE_NUM_STAGES + 1
+    stage_ev = [m.HipEvents(ns) for _ in range(K)]
+    for i in range(K):
+        step(stage_ev[i].handles)
+    torch.cuda.synchronize()
+    stage_ms = {name: float(statistics.median([stage_ev[i].elapsed_ms(s, s + 1) for i in range(K)]))
+                for s, name in enumerate(m.STAGES)}
+    log(f"# {w.name}: {K} steps, median {ms_med:.4f} ms (mean {ms_mean:.4f}, wall {1e3 * wall / K:.4f}); "
+        + " ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+
+    counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
+    work = algorithmic_work(w, counts)
+    bound, rate = BOUND[w.name]
+    fc1_s = stage_ms["fc1"] / 1e3
+    src_hash = kernel_source_hash()
+    traffic = read_traffic(w.name, src_hash)
+    if bound == "hbm":
+        achieved = work["fc1_bytes"] / fc1_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
+    else:
+        achieved = work["fc1_flops"] / fc1_s / 1e12
+        peak = MFMA_PEAK_TFLOPS[rate]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "traffic": traffic}
+    roof.update(kernel=FC1_KERNEL[w.name], kernel_ms=stage_ms["fc1"], alg_bytes_per_launch=work["fc1_bytes"],
+                alg_flops_per_launch=work["fc1_flops"], kernel_source_sha256_16=src_hash)
+    s = ms_med / 1e3
+    layer = {"alg_bytes": work["layer_bytes"], "alg_flops": work["layer_flops"],
+             "GB_per_s": work["layer_bytes"] / s / 1e9,
+             "hbm_frac": work["layer_bytes"] / s / 1e9 / HBM_PEAK_GBS,
+             "TFLOP_per_s": work["layer_flops"] / s / 1e12,
+             "active_experts": work["active_experts"], "stages_ms": stage_ms}
+    if w.act == "mxfp8":
+        # the metric's prefill fraction: whole-layer flops against the dense
+        # MX-MFMA peak at the FP8 rate, and against the FP4/FP6 rate
+        layer["mfma_frac_fp8_peak"] = layer["TFLOP_per_s"] / MFMA_PEAK_TFLOPS["fp8"]
+        layer["mfma_frac_fp4_peak"] = layer["TFLOP_per_s"] / MFMA_PEAK_TFLOPS["fp4"]
+    elif bound == "mfma":
+        layer["mfma_frac_bf16_peak"] = layer["TFLOP_per_s"] / MFMA_PEAK_TFLOPS["bf16"]
+    if w.skew:
+        top = np.sort(counts)[::-1]
+        layer["expert_histogram"] = {"top10_share": float(top[:10].sum() / counts.sum()),
+                                     "largest": top[:5].tolist(),
+                                     "empty_experts": np.flatnonzero(counts == 0).tolist()}
+    line = {
+        "metric": "MoE layer tokens/s", "value": w.T / s, "unit": "tokens/s", "ms_per_step": ms_med,
+        "ms_per_step_mean": ms_mean, "steps": K, "warmup": args.warmup,
+        "dtype": {"bf16": "bf16 x mxfp4 (bf16 MFMA, f32 acc)",
+                  "mxfp8": f"mxfp8 x {'mxfp4' if w.wfmt == 'e2m1' else 'mxfp6'} (scaled MFMA, f32 acc)"}[w.act],
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
+                   "weights": w.wfmt, "activations": w.act, "I_shared": w.I_shared},
+        "roofline": roof, "layer": layer,
+    }
+    return line, (logits, x, y, ids)
+
+
+def cpu_baseline(torch, np, gen, w, seed, logits, x, y_gpu, ntok):
+    """Time the CPU oracle (numpy float64, as it stands) on the first `ntok`
+    tokens of the workload and compare its output with the GPU's rows.  The
+    oracle's own weight quantization is input preparation, done beforehand in
+    a pool of fresh ("spawn") worker processes and not timed."""
+    from oracle import moe as om
     from oracle.routing import topk_route
+    from tests.helpers import ExpertArrays, oracle_weights, pool_workers, shutdown_pool, y_error
+
+    lg = logits[:ntok].cpu().numpy()
     ids, _ = topk_route(lg, w.k)
     experts = sorted(set(int(e) for e in ids.ravel()))
-    # fp32 weights of those experts from the same seeded generator (on the GPU),
-    # quantized by the oracle itself (not part of the timed layer)
-    mats = []
-    for e in experts:
-        mats.append(gen.expert_w1(w, e, seed, device="cuda").cpu().numpy())
-        mats.append(gen.expert_w2(w, e, seed, device="cuda").cpu().numpy())
-    shared = None
-    if w.I_shared:
-        mats.append(gen.shared_w1(w, seed, device="cuda").cpu().numpy())
-        mats.append(gen.shared_w2(w, seed, device="cuda").cpu().numpy())
-    nproc = max(1, min(16, len(os.sched_getaffinity(0))))
-    with cf.ProcessPoolExecutor(max_workers=nproc, mp_context=mp.get_context("fork")) as ex:
-        q = list(ex.map(om.quantize_weight, mats, [w.wfmt] * len(mats)))
-    per = {e: (q[2 * i][0], q[2 * i][1], q[2 * i + 1][0], q[2 * i + 1][1]) for i, e in enumerate(experts)}
-    if w.I_shared:
-        shared = (q[-2][0], q[-2][1], q[-1][0], q[-1][1])
-    arrs = tuple(ExpertArrays({e: v[i] for e, v in per.items()}, w.E) for i in range(4))
+    t0 = time.perf_counter()
+    ow = oracle_weights(w, seed, experts, fp32_on="cuda")
+    prep = time.perf_counter() - t0
+    shutdown_pool()
+    arrs = tuple(ExpertArrays({e: ow[e][i] for e in experts}, w.E) for i in range(4))
     xs = x[:ntok].to(torch.float64).cpu().numpy()
+    blas = {}
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            blas = {"library": info[0].get("internal_api"), "version": info[0].get("version"),
+                    "threads": info[0].get("num_threads")}
     except Exception:
-        threads = None
+        pass
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    ref = om.moe_forward(xs, lg, *arrs, k=w.k, wfmt=w.wfmt, act=w.act, shared=shared)
+    ref = om.moe_forward(xs, lg, *arrs, k=w.k, wfmt=w.wfmt, act=w.act)
     dt = time.perf_counter() - t0
     mr, rr = y_error(y_gpu[:ntok].float().cpu().numpy(), ref["y"])
     ids_ok = bool(np.array_equal(ids, ref["ids"]))
-    return ({"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-             "sample": f"first {ntok} tokens of {w.name} ({len(experts)} experts decoded), "
-                       f"numpy float64, {dt:.1f} s"},
+    return ({"value": ntok / dt, "unit": "tokens/s", "cores": blas.get("threads") or 1, "kind": "oracle",
+             "sample": f"first {ntok} of the {w.T} tokens of {w.name} ({len(experts)} of its active experts "
+                       f"decoded), numpy float64 in one process: {dt:.1f} s (weight quantization by the "
+                       f"oracle beforehand, {prep:.0f} s in {pool_workers()} worker processes, not timed)",
+             "affinity_cores": affinity, "cpu_model": cpu_model, "blas": blas},
             {"tokens": ntok, "max_rel": mr, "rms_rel": rr, "ids_equal": ids_ok})
 
 
@@ -225,91 +331,43 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
-    w = gen.WORKLOADS[args.workload]
-    print(f"# bench {w.name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} {w.wfmt}/{w.act} Is={w.I_shared}",
-          file=sys.stderr, flush=True)
-    logits, x, mw = build_inputs(torch, m, gen, w, args.seed)
-    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared)
-    ws = torch.empty((max(m.moe_fused_workspace_bytes(prob), 1),), dtype=torch.uint8, device="cuda")
-    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
-    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
-    wts = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
+    names = ORDER if args.workload == "all" else (args.workload,)
+    head = HEADLINE if HEADLINE in names else names[0]
+    lines = {}
+    keep = {}
+    weights = {}
+    for name in names:
+        w = gen.WORKLOADS[name]
+        key = (w.H, w.I, w.E, w.wfmt, w.I_shared)
+        if key not in weights:
+            log(f"# weights for {name}: E={w.E} H={w.H} I={w.I} {w.wfmt} I_shared={w.I_shared}")
+            weights[key] = build_weights(torch, m, gen, w, args.seed)
+        log(f"# bench {name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} {w.wfmt}/{w.act} Is={w.I_shared}")
+        lines[name], tensors = time_workload(torch, np, m, gen, w, weights[key], args)
+        if name == head:
+            keep = tensors
+        # free what later workloads do not share
+        later = {(gen.WORKLOADS[n].H, gen.WORKLOADS[n].I, gen.WORKLOADS[n].E, gen.WORKLOADS[n].wfmt,
+                  gen.WORKLOADS[n].I_shared) for n in names[names.index(name) + 1:]}
+        if key not in later:
+            del weights[key]
+            torch.cuda.empty_cache()
 
-    def step(events=None):
-        m.moe_fused(prob, x, mw, router_logits=logits, y=y, workspace=ws, topk_ids_out=ids,
-                    topk_w_out=wts, stream=stream, stage_events=events)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
-
-    ns = m.MOE_NUM_STAGES + 1
-    K = args.steps
-    # the timed steps run without instrumentation (recording the per-stage
-    # events costs about 2% of a decode step); a second, untimed pass of K
-    # steps records them for the stage breakdown and the FC1 kernel time
-    edge = m.HipEvents(2)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    edge.record(0, stream)
-    for i in range(K):
-        step()
-    edge.record(1, stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = edge.elapsed_ms(0, 1) / K
-    stage_ev = [m.HipEvents(ns) for _ in range(K)]
-    for i in range(K):
-        step(stage_ev[i].handles)
-    torch.cuda.synchronize()
-    stage_ms = {name: float(np.mean([stage_ev[i].elapsed_ms(s, s + 1) for i in range(K)]))
-                for s, name in enumerate(m.STAGES)}
-    print(f"# timed {K} steps: {ms_step:.4f} ms/step (wall {1e3 * wall / K:.4f}); stages "
-          + " ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()), file=sys.stderr, flush=True)
-
-    counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
-    work = algorithmic_work(w, counts)
-    bound, rate = BOUND[w.name]
-    fc1_s = stage_ms["fc1"] / 1e3
-    src_hash = kernel_source_hash()
-    traffic = read_traffic(w.name, src_hash)
-    if bound == "hbm":
-        achieved = work["fc1_bytes"] / fc1_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic}
-    else:
-        achieved = work["fc1_flops"] / fc1_s / 1e12
-        peak = MFMA_PEAK_TFLOPS[rate]
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "traffic": traffic}
-    roof["kernel"] = FC1_KERNEL[w.name]
-    roof["kernel_ms"] = stage_ms["fc1"]
-    roof["alg_bytes_per_launch"] = work["fc1_bytes"]
-    roof["alg_flops_per_launch"] = work["fc1_flops"]
-    roof["kernel_source_sha256_16"] = src_hash
-
-    out = {
-        "metric": "MoE layer tokens/s", "value": w.T / (ms_step / 1e3), "unit": "tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16 x mxfp4 (bf16 MFMA, f32 acc)",
-                  "mxfp8": f"mxfp8 x {'mxfp4' if w.wfmt == 'e2m1' else 'mxfp6'} (scaled MFMA, f32 acc)"}[w.act],
-        "data": "synthetic (seeded N(0,1) logits and x, N(0,0.02) weights quantized on device)",
-        "config": {"workload": w.name, "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k,
-                   "weights": w.wfmt, "activations": w.act, "I_shared": w.I_shared},
-        "roofline": roof,
-        "layer": {"alg_bytes": work["layer_bytes"], "alg_flops": work["layer_flops"],
-                  "GB_per_s": work["layer_bytes"] / (ms_step / 1e3) / 1e9,
-                  "hbm_frac": work["layer_bytes"] / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
-                  "TFLOP_per_s": work["layer_flops"] / (ms_step / 1e3) / 1e12,
-                  "active_experts": work["active_experts"], "stages_ms": stage_ms},
-    }
-    if not args.no_cpu_baseline:
-        ntok = args.cpu_sample_tokens or {"tiny_w4a16": 16, "decode_w4a16": 8, "prefill_w4a8": 4,
-                                          "skew_w4a16": 8, "w6a8_shared": 4}[w.name]
-        print(f"# cpu oracle on {ntok} tokens", file=sys.stderr, flush=True)
+    h = lines[head]
+    out = {"metric": "MoE layer tokens/s", "value": h["value"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": h["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": h["dtype"],
+           "data": "synthetic (seeded N(0,1) logits and x, N(0,0.02) weights quantized on device)",
+           "config": h["config"], "roofline": h["roofline"], "layer": h["layer"],
+           "ms_per_step_mean": h["ms_per_step_mean"],
+           "timing": "per workload: median over the timed steps of HIP-event time per moe_fused call"}
+    if len(names) > 1:
+        out["workloads"] = lines
+    if not args.no_cpu_baseline and head == HEADLINE:
+        w = gen.WORKLOADS[head]
+        logits, x, y, _ = keep
+        ntok = min(args.cpu_sample_tokens, w.T)
+        log(f"# cpu oracle on {ntok} tokens of {head}")
         cb, par = cpu_baseline(torch, np, gen, w, args.seed, logits, x, y, ntok)
         out["cpu_baseline"] = cb
         out["sampled_parity"] = par

@@ -19,8 +19,8 @@
 //    [64+16g, +16); lane l's scale byte applies to (row l%16, k block l/16).
 //
 // bf16 activations: weights are dequantized in registers with
-// v_cvt_scalef32_pk_bf16_fp4 (exact for E8M0 scales) and multiplied on the
-// bf16 MFMA.  MXFP8 activations: codes and scales feed the scaled MFMA
+// v_cvt_scalef32_pk_bf16_fp4 (E2M1) or v_cvt_scalef32_pk32_bf16_fp6 (E3M2),
+// exact for E8M0 scales, and multiplied on the bf16 MFMA.  MXFP8 activations: codes and scales feed the scaled MFMA
 // directly (TokenSpeed SiTU page, "Activation precision": MXFP8 activation x
 // MXFP4 weight; mxfp6-sm120 page: block-scaled MMA with FP32 accumulation).
 #include <hip/hip_runtime.h>
@@ -33,6 +33,8 @@ namespace moe_mx {
 namespace {
 
 constexpr int NB = 4;  // 16-column MFMA blocks per wave
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
 
 struct AFrag {
   uint4 d[4];      // bf16: 32 values; MX: d[0], d[1] = the two 16-byte code halves
@@ -88,6 +90,25 @@ __device__ __forceinline__ void mma_chunk(v4f (&acc)[NB], const AFrag& a, const 
       const int bsc = (int)((b[n].scale >> (8 * g)) & 0xffu);
       acc[n] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[n], 0, Fmt<WF>::MFMA, 0, asc,
                                                                 0, bsc);
+    }
+  } else if (WF == 2) {
+    // E3M2: the lane's 32 codes (24 bytes, element i in bits 6i..6i+5) to 32
+    // bf16 values in one conversion, exact for E8M0 scales
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const float sc = e8m0_to_f32((b[n].scale >> (8 * g)) & 0xffu);
+      const v6i src = {(int)b[n].d[0], (int)b[n].d[1], (int)b[n].d[2], (int)b[n].d[3], (int)b[n].d[4],
+                       (int)b[n].d[5]};
+      const v32bf wv = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(src, sc);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const v8bf bv = {wv[8 * s], wv[8 * s + 1], wv[8 * s + 2], wv[8 * s + 3],
+                         wv[8 * s + 4], wv[8 * s + 5], wv[8 * s + 6], wv[8 * s + 7]};
+        const uint4 ad = a.d[s];
+        v8bf av;
+        __builtin_memcpy(&av, &ad, 16);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[n], 0, 0, 0);
+      }
     }
   } else {
 #pragma unroll
@@ -296,8 +317,7 @@ static hipError_t launch_pair(const FcArgs& p, bool fc1, hipStream_t st) {
 
 hipError_t launch_fc_stream(const FcArgs& p, bool fc1, bool mx_act, int wfmt, hipStream_t st) {
   if (mx_act) return wfmt == 1 ? launch_pair<true, 1>(p, fc1, st) : launch_pair<true, 2>(p, fc1, st);
-  // bf16 activations: E2M1 weights only (checked by the host)
-  return launch_pair<false, 1>(p, fc1, st);
+  return wfmt == 1 ? launch_pair<false, 1>(p, fc1, st) : launch_pair<false, 2>(p, fc1, st);
 }
 
 }  // namespace moe_mx

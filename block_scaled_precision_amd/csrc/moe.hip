@@ -222,9 +222,11 @@ static FusedPlan plan(const moe_problem_t& p) {
     f.routed = wide ? Fc::kWide : (tiled ? Fc::kTiled : Fc::kStream);
     f.shared = shared_wide ? Fc::kWide : (shared_tiled ? Fc::kTiled : Fc::kStream);
   } else {
-    // bf16 activations (E2M1 weights): the small-M kernel, or the mid-M kernel
-    // for experts with many rows; the stream kernels when K does not fit them
-    const bool small = p.H % kSmallK == 0 && p.I % kSmallK == 0 && p.I_shared % kSmallK == 0;
+    // bf16 activations, E2M1 weights: the small-M kernel, or the mid-M kernel
+    // for experts with many rows; the stream kernels when K does not fit them.
+    // E3M2 weights take the stream kernels.
+    const bool small = p.w_fmt == MX_E2M1 && p.H % kSmallK == 0 && p.I % kSmallK == 0 &&
+                       p.I_shared % kSmallK == 0;
     const bool mid_h = small && p.H % kMidK == 0;
     const bool mid = mid_h && p.I % kMidK == 0 && f.L > 0 && f.A >= (int64_t)kMidMinRowsPerExpert * f.L && kdiv_ok;
     const bool shared_mid = mid_h && p.I_shared % kMidK == 0 && p.T >= kMidMinRowsPerExpert;
@@ -298,7 +300,6 @@ static moe_status_t validate(const moe_problem_t* p, const moe_tensors_t* t) {
   }
   // valid, but outside what the kernels implement
   if (p->w_fmt == MX_E4M3) return MOE_ERR_UNSUPPORTED;
-  if (p->w_fmt == MX_E3M2 && p->act == MOE_ACT_BF16) return MOE_ERR_UNSUPPORTED;
   if (p->H % 128 || p->I % 128 || p->I_shared % 128) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -372,6 +373,22 @@ extern "C" moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int
 extern "C" size_t moe_fused_workspace_bytes(const moe_problem_t* p) {
   if (!p || p->T < 0 || p->E < 1 || p->k < 1 || p->H <= 0 || p->I <= 0 || p->I_shared < 0) return 0;
   return plan(*p).total;
+}
+
+extern "C" size_t moe_fused_workspace_offset(const moe_problem_t* p, moe_ws_part_t part) {
+  const size_t none = ~(size_t)0;
+  if (!p || p->T < 0 || p->E < 1 || p->k < 1 || p->k > p->E || p->H <= 0 || p->I <= 0 || p->I_shared < 0)
+    return none;
+  const int L = p->local_num_experts == 0 ? p->E : p->local_num_experts;
+  if (p->local_expert_offset < 0 || L < 0 || (int64_t)p->local_expert_offset + L > p->E) return none;
+  const FusedPlan f = plan(*p);
+  switch (part) {
+    case MOE_WS_EXPERT_OFFSETS: return f.offsets;
+    case MOE_WS_SORTED_ASSIGN: return f.sorted;
+    case MOE_WS_H: return f.h;
+    case MOE_WS_H_SCALE: return p->act == MOE_ACT_MXFP8 ? f.hsc : none;
+  }
+  return none;
 }
 
 extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t, void* workspace,

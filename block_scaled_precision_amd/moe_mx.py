@@ -23,7 +23,7 @@ ACTS = {"bf16": 0, "mxfp8": 1}
 
 # Every symbol include/moe_mx.h declares.
 EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "moe_fused_workspace_bytes",
-           "moe_fused", "moe_status_str", "moe_mx_version")
+           "moe_fused", "moe_fused_workspace_offset", "moe_status_str", "moe_mx_version")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.moe_fused_workspace_bytes.restype = sz
         L.moe_fused.argtypes = [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeTensors), vp, sz, vp]
         L.moe_fused.restype = ctypes.c_int
+        L.moe_fused_workspace_offset.argtypes = [ctypes.POINTER(MoeProblem), ctypes.c_int]
+        L.moe_fused_workspace_offset.restype = sz
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_mx_version.argtypes = []
@@ -98,9 +100,35 @@ def _stream(stream):
 
 
 def _dev(*ts):
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("tensors must live on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+
+
+def _require(t, name: str, dtype, shape):
+    """The C ABI sees only a pointer: check what it will read or write."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _require_workspace(ws, need: int):
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace: expected a contiguous 1-D uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace: {ws.numel()} bytes, need {need}")
 
 
 # ------------------------------------------------------------ mx_quantize --
@@ -109,18 +137,31 @@ def mx_quantize(src: torch.Tensor, fmt: str, codes: torch.Tensor | None = None,
                 scales: torch.Tensor | None = None, stream=None):
     """Block-quantize the last axis of a bf16/fp32 matrix [rows, cols] (or a
     batch [..., rows, cols], flattened) to MX codes + E8M0 scales."""
-    _dev(src)
+    if fmt not in MX_FORMATS:
+        raise ValueError(f"unknown MX format {fmt!r}")
+    if src.dtype not in SRC_DTYPES:
+        raise ValueError(f"src: dtype {src.dtype}, expected bfloat16 or float32")
+    if src.dim() < 1:
+        raise ValueError("src: needs at least one axis")
     cols = src.shape[-1]
-    rows = src.numel() // cols if cols else 0
-    if src.stride(-1) != 1:
-        raise ValueError("last axis must be contiguous")
-    src2 = src.reshape(rows, cols) if src.is_contiguous() else src
-    ld = src2.stride(0) if src2.dim() == 2 else cols
+    if cols % 32 or cols == 0:
+        raise ValueError(f"src: last axis {cols} is not a positive multiple of 32")
+    rows = src.numel() // cols
+    if src.is_contiguous():
+        src2, ld = src.reshape(rows, cols), cols
+    elif src.dim() == 2 and src.stride(-1) == 1 and src.stride(0) >= cols:
+        src2, ld = src, src.stride(0)        # rows with a stride
+    else:
+        raise ValueError("src: must be contiguous, or 2-D with contiguous rows")
     nbytes = cols * FORMAT_BITS[fmt] // 8
+    dev = src.device
     if codes is None:
-        codes = torch.empty(src.shape[:-1] + (nbytes,), dtype=torch.uint8, device=src.device)
+        codes = torch.empty(src.shape[:-1] + (nbytes,), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty(src.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=src.device)
+        scales = torch.empty(src.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=dev)
+    _require(codes, "codes", torch.uint8, src.shape[:-1] + (nbytes,))
+    _require(scales, "scales", torch.uint8, src.shape[:-1] + (cols // 32,))
+    _dev(src, codes, scales)
     _check(lib().mx_quantize(_ptr(src2), SRC_DTYPES[src.dtype], rows, cols, ld, MX_FORMATS[fmt],
                              _ptr(codes), _ptr(scales), _stream(stream)), "mx_quantize")
     return codes, scales
@@ -135,8 +176,12 @@ def moe_route_workspace_bytes(T: int, E: int, k: int) -> int:
 def moe_route(logits: torch.Tensor, k: int, workspace: torch.Tensor | None = None, stream=None):
     """-> (topk_ids [T,k] int32, topk_w [T,k] fp32, expert_offsets [E+1] int32,
     sorted_assign [T*k] int32)."""
-    _dev(logits)
+    if logits.dim() != 2:
+        raise ValueError("logits: expected [T, E]")
     T, E = logits.shape
+    _require(logits, "logits", torch.float32, (T, E))
+    if not 1 <= k <= E:
+        raise ValueError(f"k = {k} outside [1, E = {E}]")
     dev = logits.device
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -145,7 +190,9 @@ def moe_route(logits: torch.Tensor, k: int, workspace: torch.Tensor | None = Non
     need = moe_route_workspace_bytes(T, E, k)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    _check(lib().moe_route(_ptr(logits.contiguous()), T, E, k, _ptr(ids), _ptr(w), _ptr(off), _ptr(sa),
+    _require_workspace(workspace, need)
+    _dev(logits, workspace)
+    _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _ptr(off), _ptr(sa),
                            _ptr(workspace), workspace.numel(), _stream(stream)), "moe_route")
     return ids, w, off, sa
 
@@ -175,6 +222,68 @@ def moe_fused_workspace_bytes(problem: MoeProblem) -> int:
     return lib().moe_fused_workspace_bytes(ctypes.byref(problem))
 
 
+WS_PARTS = {"expert_offsets": 0, "sorted_assign": 1, "h": 2, "h_scale": 3}
+
+
+def moe_fused_workspace_offset(problem: MoeProblem, part: str):
+    """Byte offset of an intermediate of moe_fused in its workspace, or None."""
+    off = lib().moe_fused_workspace_offset(ctypes.byref(problem), WS_PARTS[part])
+    return None if off == ctypes.c_size_t(-1).value else off
+
+
+_FMT_NAMES = {v: k for k, v in MX_FORMATS.items()}
+
+
+def check_fused_args(problem: MoeProblem, x, weights, router_logits=None, topk_ids_in=None,
+                     topk_w_in=None, y=None, workspace=None, topk_ids_out=None, topk_w_out=None):
+    """Every tensor of a moe_fused call against the problem: dtype, exact shape,
+    contiguity, one GPU.  Raises ValueError before anything reaches the ABI."""
+    p = problem
+    T, H, I, E, k, Is = p.T, p.H, p.I, p.E, p.k, p.I_shared
+    if p.w_fmt not in _FMT_NAMES or _FMT_NAMES[p.w_fmt] not in ("e2m1", "e3m2"):
+        raise ValueError(f"problem: weight format code {p.w_fmt} is not e2m1 or e3m2")
+    if weights.fmt != _FMT_NAMES[p.w_fmt]:
+        raise ValueError(f"weights are {weights.fmt}, the problem says {_FMT_NAMES[p.w_fmt]}")
+    if min(T, H, I, E, k, Is) < 0 or H == 0 or I == 0 or E == 0 or k == 0:
+        raise ValueError("problem: negative or zero size")
+    if H % 32 or I % 32 or Is % 32:
+        raise ValueError("problem: H, I and I_shared must be multiples of 32")
+    L = p.local_num_experts or E
+    b = FORMAT_BITS[weights.fmt]
+    _require(x, "x", torch.bfloat16, (T, H))
+    _require(y, "y", torch.bfloat16, (T, H))
+    if (topk_ids_in is None) != (topk_w_in is None):
+        raise ValueError("topk_ids_in and topk_w_in go together")
+    if topk_ids_in is None:
+        if router_logits is None:
+            raise ValueError("need router_logits or a precomputed top-k")
+        _require(router_logits, "router_logits", torch.float32, (T, E))
+    else:
+        _require(topk_ids_in, "topk_ids_in", torch.int32, (T, k))
+        _require(topk_w_in, "topk_w_in", torch.float32, (T, k))
+        if router_logits is not None:
+            _require(router_logits, "router_logits", torch.float32, (T, E))
+    _require(weights.w1, "w1", torch.uint8, (L, 2 * I, H * b // 8))
+    _require(weights.w1_scale, "w1_scale", torch.uint8, (L, 2 * I, H // 32))
+    _require(weights.w2, "w2", torch.uint8, (L, H, I * b // 8))
+    _require(weights.w2_scale, "w2_scale", torch.uint8, (L, H, I // 32))
+    shared = (weights.ws1, weights.ws1_scale, weights.ws2, weights.ws2_scale)
+    if Is > 0:
+        _require(weights.ws1, "ws1", torch.uint8, (2 * Is, H * b // 8))
+        _require(weights.ws1_scale, "ws1_scale", torch.uint8, (2 * Is, H // 32))
+        _require(weights.ws2, "ws2", torch.uint8, (H, Is * b // 8))
+        _require(weights.ws2_scale, "ws2_scale", torch.uint8, (H, Is // 32))
+    else:
+        shared = ()
+    if topk_ids_out is not None:
+        _require(topk_ids_out, "topk_ids_out", torch.int32, (T, k))
+    if topk_w_out is not None:
+        _require(topk_w_out, "topk_w_out", torch.float32, (T, k))
+    _require_workspace(workspace, moe_fused_workspace_bytes(p))
+    _dev(x, y, router_logits, topk_ids_in, topk_w_in, weights.w1, weights.w1_scale, weights.w2,
+         weights.w2_scale, *shared, topk_ids_out, topk_w_out, workspace)
+
+
 def moe_fused(problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, router_logits=None,
               topk_ids_in=None, topk_w_in=None, y=None, workspace=None, topk_ids_out=None,
               topk_w_out=None, stream=None, stage_events=None):
@@ -182,12 +291,13 @@ def moe_fused(problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, router_
 
     stage_events: optional ctypes array of MOE_NUM_STAGES + 1 hipEvent_t
     handles (see HipEvents) recorded at the stage boundaries."""
-    _dev(x, router_logits, topk_ids_in, topk_w_in, weights.w1, weights.w2)
     if y is None:
         y = torch.empty((problem.T, problem.H), dtype=torch.bfloat16, device=x.device)
+    need = moe_fused_workspace_bytes(problem)
     if workspace is None:
-        workspace = torch.empty((max(moe_fused_workspace_bytes(problem), 1),), dtype=torch.uint8,
-                                device=x.device)
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    check_fused_args(problem, x, weights, router_logits, topk_ids_in, topk_w_in, y, workspace,
+                     topk_ids_out, topk_w_out)
     t = MoeTensors(*(None if v is None else v.data_ptr() for v in (
         x, router_logits, topk_ids_in, topk_w_in, weights.w1, weights.w1_scale, weights.w2,
         weights.w2_scale, weights.ws1, weights.ws1_scale, weights.ws2, weights.ws2_scale, y,

@@ -15,7 +15,9 @@
  *      requantized to MXFP8 along I (MXFP8 activations);
  *   6. FC2: h times W2, fp32 accumulation;
  *   7. y[t] = sum_j w[t,j] * FC2 output of (t, j), plus an optional shared
- *      expert with its own weight, rounded once to bf16.
+ *      expert with its own weight: each weighted expert row is rounded to
+ *      bf16, the rows are summed in fp32 and the sum is rounded to bf16
+ *      (two roundings; see moe_fused below).
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers on the current HIP device; the
@@ -33,7 +35,10 @@
  *   - Device trust boundary: contents of device buffers are not inspected on
  *     the host.  Expert ids outside [0, E), non-finite inputs and NaN scale
  *     codes (255) give unspecified results (but no out-of-bounds access for
- *     ids: ids outside the local shard are skipped).
+ *     ids: ids outside the local shard are skipped).  The k expert ids of one
+ *     token must be distinct (moe_route always produces distinct ids); a
+ *     precomputed top-k that repeats an id for a token gives an unspecified
+ *     output row for that token (still no out-of-bounds access).
  *
  * Canonical MX layouts (element codes along the contraction axis K):
  *   E2M1: two codes per byte, element 2j in bits 0-3, element 2j+1 in bits 4-7;
@@ -188,10 +193,37 @@ enum {
  * j = 0..k-1, then the shared expert's row (scaled and rounded the same way);
  * results are deterministic from run to run.
  * Workspace: at least moe_fused_workspace_bytes(p) bytes, 256-byte aligned.
+ * Its contents need not be initialised; nothing in it is read before this
+ * call writes it.
  */
 size_t moe_fused_workspace_bytes(const moe_problem_t* p);
 moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_fused_workspace_offset -- where moe_fused leaves an intermediate result
+ * in its workspace, for inspection after the stream has reached the end of
+ * the call (housekeeping: testing and debugging; the layer's steps are those
+ * listed at the top of this file).  Returns the byte offset from the start of
+ * the workspace, or (size_t)-1 for an invalid problem or a part the problem
+ * does not have.  Parts (L = local experts, A = T*k):
+ *   MOE_WS_EXPERT_OFFSETS  int32 [L+1]: exclusive prefix sum of the per-local-
+ *                          expert assignment counts (step 2);
+ *   MOE_WS_SORTED_ASSIGN   int32 [A]: assignment ids t*k + j of the local
+ *                          experts ordered by (expert, token); entries from
+ *                          offsets[L] on are unused;
+ *   MOE_WS_H               the FC2 input of permuted row p (step 5), rows of I
+ *                          values: bf16 (bf16 activations) or E4M3 codes
+ *                          (MXFP8 activations), [A, I] row-major;
+ *   MOE_WS_H_SCALE         E8M0 scales of MOE_WS_H, [A, I/32] (MXFP8 only).
+ */
+typedef enum {
+  MOE_WS_EXPERT_OFFSETS = 0,
+  MOE_WS_SORTED_ASSIGN = 1,
+  MOE_WS_H = 2,
+  MOE_WS_H_SCALE = 3
+} moe_ws_part_t;
+size_t moe_fused_workspace_offset(const moe_problem_t* p, moe_ws_part_t part);
 
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_str(moe_status_t s);

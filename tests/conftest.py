@@ -23,3 +23,10 @@ def has_gpu():
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # join the oracle process pool, if a test started one
+    helpers = sys.modules.get("tests.helpers")
+    if helpers is not None:
+        helpers.shutdown_pool()

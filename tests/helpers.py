@@ -69,50 +69,119 @@ def gpu_weights(w: gen.Workload, seed: int = 0, experts=None, device="cuda", fp3
 
 # --------------------------------------------------------- oracle side ----
 
-def _oracle_quantize(arr: np.ndarray, fmt: str):
-    from oracle import moe as om
-    return om.quantize_weight(arr.astype(np.float64), fmt)
+from tests.oracle_jobs import ExpertArrays, partial_job, quantize_job  # noqa: E402
+
+_POOL = None
 
 
-def oracle_weights(w: gen.Workload, seed: int = 0, experts=None, fp32_on="cpu", workers=None):
+def pool_workers() -> int:
+    """Pool size: the CPUs this process may run on, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def pool() -> cf.ProcessPoolExecutor:
+    """One process pool for the oracle jobs, started with "spawn": its workers
+    are fresh interpreters that import only numpy and the oracle, so nothing
+    is forked from a process that has initialised HIP."""
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ProcessPoolExecutor(max_workers=pool_workers(), mp_context=mp.get_context("spawn"))
+    return _POOL
+
+
+def shutdown_pool():
+    global _POOL
+    if _POOL is not None:
+        _POOL.shutdown(wait=True, cancel_futures=True)
+        _POOL = None
+
+
+def _bounded_map(fn, jobs, in_flight):
+    """fn over the jobs in the pool, keeping at most `in_flight` submitted
+    (each job may carry a large array); results in job order."""
+    ex = pool()
+    out = [None] * len(jobs)
+    pending = {}
+    it = iter(enumerate(jobs))
+    for i, job in it:
+        pending[ex.submit(fn, job)] = i
+        if len(pending) >= in_flight:
+            done, _ = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+            for f in done:
+                out[pending.pop(f)] = f.result()
+    for f in cf.as_completed(list(pending)):
+        out[pending.pop(f)] = f.result()
+    return out
+
+
+def oracle_weights(w: gen.Workload, seed: int = 0, experts=None, fp32_on="cpu", cache=None):
     """Quantize the fp32 weights of the listed experts with the oracle.
 
     Returns dict expert -> (w1, s1, w2, s2) numpy arrays, plus "shared" when
-    the workload has a shared expert.
+    the workload has a shared expert.  `cache` (a dict) keeps results across
+    calls for workloads with the same weight shapes and seed.
     """
     ids = list(range(w.E)) if experts is None else list(experts)
-    jobs = []
-    for e in ids:
-        jobs.append((e, "w1", gen.expert_w1(w, e, seed, device=fp32_on).cpu().numpy()))
-        jobs.append((e, "w2", gen.expert_w2(w, e, seed, device=fp32_on).cpu().numpy()))
     if w.I_shared:
-        jobs.append(("shared", "w1", gen.shared_w1(w, seed, device=fp32_on).cpu().numpy()))
-        jobs.append(("shared", "w2", gen.shared_w2(w, seed, device=fp32_on).cpu().numpy()))
-    big = sum(j[2].size for j in jobs) > 4_000_000
-    res = {}
-    if big:
-        nw = workers or min(8, os.cpu_count() or 1, len(jobs))
-        # fork: the workers only run numpy and never touch the GPU
-        with cf.ProcessPoolExecutor(max_workers=nw, mp_context=mp.get_context("fork")) as ex:
-            outs = list(ex.map(_oracle_quantize, [j[2] for j in jobs], [w.wfmt] * len(jobs)))
+        ids.append("shared")
+    cache = {} if cache is None else cache
+    key = lambda e: (w.H, w.I, w.E, w.I_shared, w.wfmt, seed, e)  # noqa: E731
+    todo = [e for e in ids if key(e) not in cache]
+
+    def mats(e):
+        if e == "shared":
+            return (gen.shared_w1(w, seed, device=fp32_on).cpu().numpy(),
+                    gen.shared_w2(w, seed, device=fp32_on).cpu().numpy())
+        return (gen.expert_w1(w, e, seed, device=fp32_on).cpu().numpy(),
+                gen.expert_w2(w, e, seed, device=fp32_on).cpu().numpy())
+
+    values = sum(3 * (w.I_shared if e == "shared" else w.I) * w.H for e in todo)
+    if values <= 4_000_000:
+        for e in todo:
+            a, b = mats(e)
+            cache[key(e)] = quantize_job((a, w.wfmt)) + quantize_job((b, w.wfmt))
     else:
-        outs = [_oracle_quantize(j[2], w.wfmt) for j in jobs]
-    for (e, kind, _), (p, s) in zip(jobs, outs):
-        res.setdefault(e, {})[kind] = (p, s)
-    return {e: (d["w1"][0], d["w1"][1], d["w2"][0], d["w2"][1]) for e, d in res.items()}
+        # fp32 matrices are drawn lazily, a bounded number in flight
+        ex = pool()
+        limit = 2 * pool_workers()
+        pending = {}
+        res = {e: [None, None] for e in todo}
+
+        def drain(block):
+            done, _ = cf.wait(pending, return_when=cf.FIRST_COMPLETED if block else cf.ALL_COMPLETED)
+            for f in done:
+                e, part = pending.pop(f)
+                res[e][part] = f.result()
+
+        for e in todo:
+            for part, m in enumerate(mats(e)):
+                pending[ex.submit(quantize_job, (m, w.wfmt))] = (e, part)
+                if len(pending) >= limit:
+                    drain(True)
+        while pending:
+            drain(False)
+        for e, (q1, q2) in res.items():
+            cache[key(e)] = q1 + q2
+    return {e: cache[key(e)] for e in ids}
 
 
-class ExpertArrays:
-    """Indexable stand-in for an [E, ...] array holding only some experts;
-    indexing a missing expert raises KeyError."""
-
-    def __init__(self, per_expert: dict, E: int):
-        self._d = per_expert
-        some = next(iter(per_expert.values()))
-        self.shape = (E,) + some.shape
-
-    def __getitem__(self, e):
-        return self._d[int(e)]
+def oracle_rows(w: gen.Workload, x_rows: torch.Tensor, ids: np.ndarray, wts: np.ndarray, seed: int = 0,
+                fp32_on="cpu", cache=None, shared_weight: float = 1.0) -> np.ndarray:
+    """Oracle layer output (float64) for the given token rows, computed as one
+    job per expert shard (and one for the shared expert) in the pool and
+    summed in the oracle's own order.  x_rows [n, H] bf16; ids / wts [n, k]:
+    the oracle's routing of those tokens."""
+    experts = sorted(set(int(e) for e in np.asarray(ids).ravel()))
+    ow = oracle_weights(w, seed, experts, fp32_on=fp32_on, cache=cache)
+    xs = x_rows.to(torch.float64).cpu().numpy()
+    jobs = [(e, ow[e], None, 1.0, xs, ids, wts, w.E, w.k, w.wfmt, w.act) for e in experts]
+    if w.I_shared:
+        jobs.append((-1, None, ow["shared"], shared_weight, xs, ids, wts, w.E, w.k, w.wfmt, w.act))
+    parts = _bounded_map(partial_job, jobs, 2 * pool_workers())
+    y = np.zeros((xs.shape[0], w.H), dtype=np.float64)
+    for _, part in parts:  # ascending expert, then the shared expert
+        y += part
+    return y
 
 
 def oracle_arrays(ow: dict, E: int):

@@ -65,7 +65,7 @@ def _tensors(m, **kw):
     (dict(E=0), 1), (dict(E=1025), 1), (dict(k=0), 1), (dict(k=9), 1),
     (dict(off=4, cnt=8), 1), (dict(off=-1), 1), (dict(I_shared=-32), 1),
     (dict(H=160), 2), (dict(I=96), 2), (dict(I_shared=64), 2), (dict(I_shared=48), 1),
-    (dict(fmt="e4m3"), 2), (dict(fmt="e3m2", act="bf16"), 2),
+    (dict(fmt="e4m3"), 2),
 ])
 def test_invalid_problems_rejected_on_host(change, status):
     m, L = _lib()
