@@ -147,11 +147,16 @@ def oracle_weights(w: gen.Workload, seed: int = 0, experts=None, fp32_on="cpu", 
         pending = {}
         res = {e: [None, None] for e in todo}
 
+        finished = [0]
+
         def drain(block):
             done, _ = cf.wait(pending, return_when=cf.FIRST_COMPLETED if block else cf.ALL_COMPLETED)
             for f in done:
                 e, part = pending.pop(f)
                 res[e][part] = f.result()
+                finished[0] += 1
+                if finished[0] % 64 == 0:
+                    print_flush(f"  oracle quantized {finished[0]} of {2 * len(todo)} weight matrices")
 
         for e in todo:
             for part, m in enumerate(mats(e)):
