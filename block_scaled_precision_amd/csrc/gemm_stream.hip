@@ -274,7 +274,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const uint8_t* bsrow[NB];
 #pragma unroll
   for (int n = 0; n < NB; ++n) {
-    const int row = col0 + 16 * n + r;
+    // columns past N (a dense GEMM with N % 64 != 0) read the last weight
+    // row and are not stored
+    const int row = min(col0 + 16 * n + r, H - 1);
     brow[n] = wb + (int64_t)row * wrow;
     bsrow[n] = sb + (int64_t)row * (K / 32);
   }
@@ -300,7 +302,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
     uint16_t* o = p.obuf + orow * H + col0 + r;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) o[16 * n] = f32_to_bf16_rne(w * acc[n][i]);
+    for (int n = 0; n < NB; ++n)
+      if (col0 + 16 * n + r < H) o[16 * n] = f32_to_bf16_rne(w * acc[n][i]);
   }
 }
 

@@ -375,6 +375,108 @@ extern "C" size_t moe_fused_workspace_bytes(const moe_problem_t* p) {
   return plan(*p).total;
 }
 
+// ----------------------------------------------------------- dense GEMM --
+
+// Kernel and M-tile height of a dense GEMM C[M, N] = A W^T with K = K on the
+// FC2 instantiations (bf16 rows of dense_weight * A W^T): the families that
+// the layer's shared expert takes, where N fits their N-blocks; the stream
+// kernels (16-row tiles, N masked to a multiple of 8) otherwise.
+static Fc dense_kind(int64_t M, int64_t N, int64_t K, bool mx, mx_elem_t wf, int grid, int* rows) {
+  *rows = kStreamRows;
+  if (mx) {
+    if (M >= kTiledMinRowsPerExpert && K % kTiledKMultiple == 0) {
+      if (wf == MX_E2M1 && K % 512 == 0 && K >= 1024 && N % kWideCols == 0 && (double)M * K < 4294967296.0) {
+        *rows = kTiledRows;
+        return Fc::kWide;
+      }
+      const int r = dense_tiled_rows((int)M, (int)N, false, grid);
+      for (const int rr : {r, r == kTiledRows ? kTiledRowsLow : kTiledRows}) {
+        if (N % tiled_weight_rows(rr) == 0) {
+          *rows = rr;
+          return Fc::kTiled;
+        }
+      }
+    }
+    return Fc::kStream;
+  }
+  if (wf == MX_E2M1) {
+    if (M >= kMidMinRowsPerExpert && K % kMidK == 0 && N % kWideCols == 0) {
+      *rows = M >= kMidHighMinRowsPerExpert ? kMidRowsHigh : kMidRows;
+      return Fc::kMid;
+    }
+    if (K % kSmallK == 0 && N % kSmallColsFc2 == 0) return Fc::kSmall;
+  }
+  return Fc::kStream;
+}
+
+extern "C" size_t mx_gemm_workspace_bytes(int64_t M, int64_t K, moe_act_t act) {
+  if (M < 0 || K <= 0 || K % 32) return 0;
+  if (act != MOE_ACT_MXFP8) return 0;
+  return align_up((size_t)(M * K), 256) + align_up((size_t)(M * K / 32), 256);
+}
+
+extern "C" moe_status_t mx_gemm(const void* a, const uint8_t* a_scale, int64_t M, int64_t N, int64_t K,
+                                moe_act_t act, const uint8_t* w, const uint8_t* w_scale, mx_elem_t w_fmt,
+                                float alpha, void* c, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (M < 0 || N <= 0 || K <= 0 || K % 32) return MOE_ERR_INVALID_ARG;
+  if (act != MOE_ACT_BF16 && act != MOE_ACT_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (w_fmt != MX_E2M1 && w_fmt != MX_E3M2 && w_fmt != MX_E4M3) return MOE_ERR_INVALID_ARG;
+  if (act == MOE_ACT_BF16 && a_scale) return MOE_ERR_INVALID_ARG;
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || (double)M * N > 9.0e15) return MOE_ERR_INVALID_ARG;
+  if (M > 0) {
+    if (!a || !w || !w_scale || !c) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(a) || !aligned16(w) || !aligned16(c) || (a_scale && !aligned16(a_scale)))
+      return MOE_ERR_INVALID_ARG;
+  }
+  if (w_fmt == MX_E4M3 || N % 8 || K % 128) return MOE_ERR_UNSUPPORTED;
+  const bool quant = act == MOE_ACT_MXFP8 && !a_scale;
+  const size_t need = quant ? mx_gemm_workspace_bytes(M, K, act) : 0;
+  if (quant && (workspace_bytes < need || !workspace)) return MOE_ERR_WORKSPACE;
+  if (quant && ((uintptr_t)workspace & 255u) != 0) return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  moe_status_t st = check_arch();
+  if (st != MOE_OK) return st;
+
+  const bool mx = act == MOE_ACT_MXFP8;
+  const uint8_t* codes = (const uint8_t*)a;
+  const uint8_t* scales = a_scale;
+  if (quant) {
+    uint8_t* qc = (uint8_t*)workspace;
+    uint8_t* qs = qc + align_up((size_t)(M * K), 256);
+    if (launch_quantize(a, MOE_SRC_BF16, M, K, K, MX_E4M3, qc, qs, stream) != hipSuccess) return MOE_ERR_HIP;
+    codes = qc;
+    scales = qs;
+  }
+  const int cus = device_cus();
+  const int tgrid = cus < 8 ? 8 : cus & ~7;
+  int rows = 0;
+  const Fc kind = dense_kind(M, N, K, mx, w_fmt, tgrid, &rows);
+  FcArgs g = {};
+  g.dense_rows = (int)M;
+  g.dense_weight = alpha;
+  g.k = 1;
+  g.a = mx ? (const void*)codes : a;
+  g.a_scale = scales;
+  g.w = w;
+  g.w_scale = w_scale;
+  g.K = (int)K;
+  g.N = (int)N;
+  const int cols = fc_cols(kind, false, rows);
+  g.nchunks = (int)((N + cols - 1) / cols);  // the stream kernels mask the last chunk's columns
+  g.obuf = (uint16_t*)c;
+  const int wf = w_fmt == MX_E2M1 ? 1 : 2;
+  hipError_t e = hipSuccess;
+  switch (kind) {
+    case Fc::kSmall: e = launch_fc_small(g, false, cus, stream); break;
+    case Fc::kMid: e = launch_fc_mid(g, false, rows, cus, stream); break;
+    case Fc::kWide: e = launch_fc_wide(g, false, cus, stream); break;
+    case Fc::kTiled: e = launch_fc_tiled(g, false, wf, rows, cus, stream); break;
+    default: e = launch_fc_stream(g, false, mx, wf, stream); break;
+  }
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 extern "C" size_t moe_fused_workspace_offset(const moe_problem_t* p, moe_ws_part_t part) {
   const size_t none = ~(size_t)0;
   if (!p || p->T < 0 || p->E < 1 || p->k < 1 || p->k > p->E || p->H <= 0 || p->I <= 0 || p->I_shared < 0)

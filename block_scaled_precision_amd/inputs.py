@@ -109,6 +109,22 @@ def shared_w2(w: Workload, seed: int = 0, device="cpu") -> torch.Tensor:
     return normal((w.H, w.I_shared), seed, SW2, device=device, std=0.02)
 
 
+def random_bytes(shape, seed: int, tensor: int, index: int = 0) -> torch.Tensor:
+    """Uniform random bytes (uint8, CPU).  Read as packed E2M1 or E3M2 codes
+    every field is a finite element code, so they serve as weights whose codes
+    are drawn directly."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_of(seed, tensor, index))
+    return torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
+
+
+def small_integers(shape, seed: int, tensor: int, lo: int = -8, hi: int = 8) -> torch.Tensor:
+    """Integers uniform in [lo, hi] as bf16 (exact), CPU."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_of(seed, tensor))
+    return torch.randint(lo, hi + 1, shape, generator=g).to(torch.bfloat16)
+
+
 def scaled(w: Workload, **changes) -> Workload:
     """Same workload with some sizes replaced (for small parity cases)."""
     d = dict(w.__dict__)

@@ -22,8 +22,9 @@ SRC_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 ACTS = {"bf16": 0, "mxfp8": 1}
 
 # Every symbol include/moe_mx.h declares.
-EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "moe_fused_workspace_bytes",
-           "moe_fused", "moe_fused_workspace_offset", "moe_status_str", "moe_mx_version")
+EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "mx_gemm_workspace_bytes", "mx_gemm",
+           "moe_fused_workspace_bytes", "moe_fused", "moe_fused_workspace_offset", "moe_status_str",
+           "moe_mx_version")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +71,11 @@ def lib() -> ctypes.CDLL:
         L.moe_fused_workspace_bytes.restype = sz
         L.moe_fused.argtypes = [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeTensors), vp, sz, vp]
         L.moe_fused.restype = ctypes.c_int
+        L.mx_gemm_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
+        L.mx_gemm_workspace_bytes.restype = sz
+        L.mx_gemm.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp,
+                              sz, vp]
+        L.mx_gemm.restype = ctypes.c_int
         L.moe_fused_workspace_offset.argtypes = [ctypes.POINTER(MoeProblem), ctypes.c_int]
         L.moe_fused_workspace_offset.restype = sz
         L.moe_status_str.argtypes = [ctypes.c_int]
@@ -195,6 +201,51 @@ def moe_route(logits: torch.Tensor, k: int, workspace: torch.Tensor | None = Non
     _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _ptr(off), _ptr(sa),
                            _ptr(workspace), workspace.numel(), _stream(stream)), "moe_route")
     return ids, w, off, sa
+
+
+# ---------------------------------------------------------------- gemm ---
+
+def mx_gemm_workspace_bytes(M: int, K: int, act: str) -> int:
+    return lib().mx_gemm_workspace_bytes(M, K, ACTS[act])
+
+
+def mx_gemm(a: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor, fmt: str, act: str = "mxfp8",
+            a_scale: torch.Tensor | None = None, alpha: float = 1.0, c: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """C [M, N] bf16 = alpha * A W^T over MX weights w [N, K*b/8] + w_scale
+    [N, K/32].  a: [M, K] bf16 (act "bf16", or "mxfp8" quantized on the
+    device), or E4M3 codes [M, K] uint8 with a_scale [M, K/32] (act "mxfp8")."""
+    if fmt not in ("e2m1", "e3m2"):
+        raise ValueError(f"weight format {fmt!r} is not e2m1 or e3m2")
+    if act not in ACTS:
+        raise ValueError(f"unknown activation precision {act!r}")
+    if a.dim() != 2 or w.dim() != 2:
+        raise ValueError("a and w must be 2-D")
+    M, K = a.shape
+    N = w.shape[0]
+    b = FORMAT_BITS[fmt]
+    if a_scale is None:
+        _require(a, "a", torch.bfloat16, (M, K))
+    else:
+        if act != "mxfp8":
+            raise ValueError("a_scale goes with act='mxfp8'")
+        _require(a, "a", torch.uint8, (M, K))
+        _require(a_scale, "a_scale", torch.uint8, (M, K // 32))
+    _require(w, "w", torch.uint8, (N, K * b // 8))
+    _require(w_scale, "w_scale", torch.uint8, (N, K // 32))
+    if c is None:
+        c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _require(c, "c", torch.bfloat16, (M, N))
+    need = mx_gemm_workspace_bytes(M, K, act) if a_scale is None else 0
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+    if workspace is not None:
+        _require_workspace(workspace, need)
+    _dev(a, a_scale, w, w_scale, c, workspace)
+    _check(lib().mx_gemm(_ptr(a), _ptr(a_scale), M, N, K, ACTS[act], _ptr(w), _ptr(w_scale), MX_FORMATS[fmt],
+                         alpha, _ptr(c), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                         _stream(stream)), "mx_gemm")
+    return c
 
 
 # ---------------------------------------------------------------- fused --

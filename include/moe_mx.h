@@ -128,6 +128,36 @@ moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int
                        float* topk_w, int32_t* expert_offsets, int32_t* sorted_assign,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * mx_gemm -- dense MX GEMM with bf16 output (mxfp6-sm120 page, table of
+ * paths, "Dense" row; "Execution model" figure: bf16 activations quantized
+ * on the device to E4M3 with one UE8M0 scale per 32 K values, packed MX
+ * weights with one UE8M0 scale per 32 K values, FP32 accumulation, bf16
+ * output; "Validated scope": M > 0, N % 8 == 0, K % 128 == 0).
+ *
+ *   C[m, n] = bf16_RNE(alpha * sum_k A'[m, k] * W'[n, k])   (fp32 accumulation)
+ *
+ * a        act == MOE_ACT_BF16: [M, K] bf16, rows contiguous; multiplied as
+ *          given (W4A16 / W6A16).
+ *          act == MOE_ACT_MXFP8 and a_scale == NULL: [M, K] bf16, quantized
+ *          on the device to E4M3 + E8M0 per 32 along K into the workspace
+ *          (W4A8 / W6A8), exactly as mx_quantize does.
+ *          act == MOE_ACT_MXFP8 and a_scale != NULL: [M, K] E4M3 codes with
+ *          scales a_scale [M, K/32] (e.g. from mx_quantize); no workspace.
+ * w, w_scale  [N, K*b/8] packed codes and [N, K/32] E8M0 scales of w_fmt
+ *          (MX_E2M1 or MX_E3M2), the canonical layout above.
+ * c        [M, N] bf16 out, rows contiguous.
+ * workspace   at least mx_gemm_workspace_bytes(M, K, act) bytes (0 unless A
+ *          is quantized here), 256-byte aligned; contents need not be set.
+ * Requires M >= 0 (0: no-op), K % 32 == 0, 16-byte aligned a, c, w (and
+ * a_scale if given); N % 8 != 0, K % 128 != 0 or E4M3 weights give
+ * MOE_ERR_UNSUPPORTED.  Deterministic.
+ */
+size_t mx_gemm_workspace_bytes(int64_t M, int64_t K, moe_act_t act);
+moe_status_t mx_gemm(const void* a, const uint8_t* a_scale, int64_t M, int64_t N, int64_t K, moe_act_t act,
+                     const uint8_t* w, const uint8_t* w_scale, mx_elem_t w_fmt, float alpha, void* c,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Problem description of one fused MoE layer call. */
 typedef struct {
   int32_t T;                   /* tokens (>= 0)                                      */

@@ -131,3 +131,30 @@ def test_valid_call_without_gfx950_fails_closed():
     p = _problem(m)
     t = _tensors(m)
     assert L.moe_fused(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(1 << 20), 1 << 40, None) == 4
+
+
+def test_gemm_validation():
+    m, L = _lib()
+    vp = ctypes.c_void_p
+    a = vp(1 << 20)
+    f = ctypes.c_float(1.0)
+    # (a, a_scale, M, N, K, act, w, w_scale, fmt, alpha, c, ws, ws_bytes, stream)
+    call = lambda *args: L.mx_gemm(*args)  # noqa: E731
+    assert call(a, None, 4, 64, 100, 0, a, a, 1, f, a, None, 0, None) == 1        # K % 32
+    assert call(a, None, -1, 64, 128, 0, a, a, 1, f, a, None, 0, None) == 1       # M < 0
+    assert call(a, None, 4, 0, 128, 0, a, a, 1, f, a, None, 0, None) == 1         # N = 0
+    assert call(a, None, 4, 64, 128, 5, a, a, 1, f, a, None, 0, None) == 1        # bad act
+    assert call(a, None, 4, 64, 128, 0, a, a, 9, f, a, None, 0, None) == 1        # bad format
+    assert call(a, a, 4, 64, 128, 0, a, a, 1, f, a, None, 0, None) == 1           # scales with bf16
+    assert call(None, None, 4, 64, 128, 0, a, a, 1, f, a, None, 0, None) == 1     # null A
+    assert call(vp((1 << 20) + 2), None, 4, 64, 128, 0, a, a, 1, f, a, None, 0, None) == 1  # misaligned
+    assert call(a, None, 4, 60, 128, 0, a, a, 1, f, a, None, 0, None) == 2        # N % 8
+    assert call(a, None, 4, 64, 96, 0, a, a, 1, f, a, None, 0, None) == 2         # K % 128
+    assert call(a, None, 4, 64, 128, 0, a, a, 3, f, a, None, 0, None) == 2        # E4M3 weights
+    assert call(a, None, 4, 64, 128, 1, a, a, 1, f, a, None, 0, None) == 3        # no workspace
+    need = L.mx_gemm_workspace_bytes(4, 128, 1)
+    assert need >= 4 * 128 + 4 * 4 and L.mx_gemm_workspace_bytes(4, 128, 0) == 0
+    assert call(a, None, 4, 64, 128, 1, a, a, 1, f, a, vp(1 << 20), need - 1, None) == 3
+    assert call(a, a, 4, 64, 128, 1, a, a, 1, f, a, None, 0, None) == 4          # pre-quantized: no workspace
+    assert call(None, None, 0, 64, 128, 0, None, None, 1, f, None, None, 0, None) == 0  # M = 0
+    assert call(a, None, 4, 64, 128, 0, a, a, 2, f, a, None, 0, None) == 4        # valid: no gfx950 here
