@@ -263,6 +263,87 @@ def time_workload(torch, np, m, gen, w, mw, args):
     return line, (logits, x, y, ids)
 
 
+def event_median(torch, m, fn, steps, warmup):
+    """Median HIP-event time (ms) of fn() over `steps` calls after `warmup`."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = m.HipEvents(steps + 1)
+    ev.record(0, stream)
+    for i in range(steps):
+        fn()
+        ev.record(i + 1, stream)
+    torch.cuda.synchronize()
+    return statistics.median([ev.elapsed_ms(i, i + 1) for i in range(steps)])
+
+
+def small_batches(torch, np, m, gen, mw, args, batches=(1, 2, 4, 8)):
+    """The decode shapes (H=7168, I=2048, E=384 resident experts, top-8, bf16
+    activations) at batches of 1 to 8 tokens: the whole layer per call, and
+    the packed weights of the experts the batch routes to (what the call must
+    stream from HBM) per second against the HBM peak."""
+    base = gen.WORKLOADS[HEADLINE]
+    out = {}
+    for T in batches:
+        w = gen.scaled(base, T=T)
+        logits = gen.router_logits(w, args.seed, device="cuda")
+        x = gen.hidden_states(w, args.seed, device="cuda")
+        prob = m.make_problem(T, w.H, w.I, w.E, w.k, w.wfmt, w.act)
+        ws = torch.empty((m.moe_fused_workspace_bytes(prob),), dtype=torch.uint8, device="cuda")
+        y = torch.empty((T, w.H), dtype=torch.bfloat16, device="cuda")
+        ids = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
+        fn = lambda: m.moe_fused(prob, x, mw, router_logits=logits, y=y, workspace=ws, topk_ids_out=ids)  # noqa: E731
+        ms = event_median(torch, m, fn, args.steps, args.warmup)
+        counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
+        work = algorithmic_work(w, counts)
+        wbytes = work["active_experts"] * (work["per_expert_w1_bytes"] + work["per_expert_w2_bytes"])
+        gbs = wbytes / (ms / 1e3) / 1e9
+        out[str(T)] = {"ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "active_experts": work["active_experts"],
+                       "weight_bytes": wbytes, "weight_GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        log(f"# decode shapes T={T}: {ms * 1e3:.1f} us, {work['active_experts']} experts, {gbs:.0f} GB/s of weights")
+    return out
+
+
+# dense GEMMs timed through mx_gemm: (name, M, N, K, weights, activations, roof)
+GEMMS = (
+    ("w4a8_8192x4096x7168", 8192, 4096, 7168, "e2m1", "mxfp8", "fp8"),
+    ("w6a8_2048x8192x5120", 2048, 8192, 5120, "e3m2", "mxfp8", "fp8"),
+    ("w4a16_8x4096x7168", 8, 4096, 7168, "e2m1", "bf16", "hbm"),
+)
+
+
+def dense_gemms(torch, m, gen, args):
+    """mx_gemm on dense shapes: the prefill FC1 shape of one expert group as
+    one GEMM (W4A8), the shared expert's FC1 (W6A8), and a decode-sized GEMV
+    (W4A16, weight-streaming bound).  The activations are quantized inside
+    the call when they are MXFP8 (part of the timed work)."""
+    out = {}
+    for name, M, N, K, fmt, act, roof in GEMMS:
+        a = gen.normal((M, K), args.seed, 30, device="cuda").to(torch.bfloat16)
+        wq, sq = m.mx_quantize(gen.normal((N, K), args.seed, 31, device="cuda", std=0.02), fmt)
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty((max(m.mx_gemm_workspace_bytes(M, K, act), 1),), dtype=torch.uint8, device="cuda")
+        fn = lambda: m.mx_gemm(a, wq, sq, fmt, act, c=c, workspace=ws)  # noqa: E731
+        ms = event_median(torch, m, fn, args.steps, args.warmup)
+        flops = 2.0 * M * N * K
+        wbytes = N * K * m.FORMAT_BITS[fmt] / 8 + N * K / 32
+        nbytes = wbytes + M * K * 2 + M * N * 2
+        d = {"M": M, "N": N, "K": K, "weights": fmt, "activations": act, "ms": ms,
+             "TFLOP_per_s": flops / (ms / 1e3) / 1e12, "GB_per_s": nbytes / (ms / 1e3) / 1e9}
+        if roof == "hbm":
+            d["roofline"] = {"bound": "hbm", "achieved": d["GB_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": d["GB_per_s"] / HBM_PEAK_GBS}
+        else:
+            d["roofline"] = {"bound": "mfma", "achieved": d["TFLOP_per_s"], "peak": MFMA_PEAK_TFLOPS[roof],
+                             "unit": "TFLOP/s", "frac": d["TFLOP_per_s"] / MFMA_PEAK_TFLOPS[roof]}
+        out[name] = d
+        log(f"# mx_gemm {name}: {ms * 1e3:.1f} us, {d['TFLOP_per_s']:.0f} TFLOP/s, {d['GB_per_s']:.0f} GB/s")
+        del a, wq, sq, c, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(torch, np, gen, w, seed, logits, x, y_gpu, ntok):
     """Time the CPU oracle (numpy float64, as it stands) on the first `ntok`
     tokens of the workload and compare its output with the GPU's rows.  The
@@ -346,6 +427,8 @@ def main():
         lines[name], tensors = time_workload(torch, np, m, gen, w, weights[key], args)
         if name == head:
             keep = tensors
+            if args.workload == "all":
+                small = small_batches(torch, np, m, gen, weights[key], args)
         # free what later workloads do not share
         later = {(gen.WORKLOADS[n].H, gen.WORKLOADS[n].I, gen.WORKLOADS[n].E, gen.WORKLOADS[n].wfmt,
                   gen.WORKLOADS[n].I_shared) for n in names[names.index(name) + 1:]}
@@ -363,6 +446,9 @@ def main():
            "timing": "per workload: median over the timed steps of HIP-event time per moe_fused call"}
     if len(names) > 1:
         out["workloads"] = lines
+    if args.workload == "all":
+        out["small_batches"] = small
+        out["dense_gemm"] = dense_gemms(torch, m, gen, args)
     if not args.no_cpu_baseline and head == HEADLINE:
         w = gen.WORKLOADS[head]
         logits, x, y, _ = keep

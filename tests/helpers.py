@@ -9,6 +9,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import multiprocessing as mp
 import os
+import sys
 
 import numpy as np
 import torch
@@ -155,8 +156,9 @@ def oracle_weights(w: gen.Workload, seed: int = 0, experts=None, fp32_on="cpu", 
                 e, part = pending.pop(f)
                 res[e][part] = f.result()
                 finished[0] += 1
-                if finished[0] % 64 == 0:
-                    print_flush(f"  oracle quantized {finished[0]} of {2 * len(todo)} weight matrices")
+                if finished[0] % 64 == 0:  # progress on stderr: bench.py's stdout is one JSON line
+                    print(f"  oracle quantized {finished[0]} of {2 * len(todo)} weight matrices",
+                          file=sys.stderr, flush=True)
 
         for e in todo:
             for part, m in enumerate(mats(e)):
