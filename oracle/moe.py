@@ -46,6 +46,33 @@ def silu(g: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g))
 
 
+# SwiGLU-OAI constants (the gpt-oss gated activation): the gate is clipped
+# from above and the up projection on both sides at this limit, and the
+# sigmoid takes the gate scaled by this slope.
+OAI_LIMIT = 7.0
+OAI_ALPHA = 1.702
+
+
+def gated(g: np.ndarray, u: np.ndarray, act_fn: str = "silu") -> np.ndarray:
+    """The gated activation of FC1's two halves, float64 ("b12x" page, "What's
+    in here", MoE: SiLU, ReLU2 and SwiGLU-OAI activations):
+      silu        SiLU(g) * u
+      relu2       max(g, 0)**2 * u
+      swiglu_oai  (clip(u, -L, L) + 1) * g' / (1 + exp(-alpha g')),
+                  g' = min(g, L), L = 7, alpha = 1.702."""
+    if act_fn == "silu":
+        return silu(g) * u
+    if act_fn == "relu2":
+        r = np.maximum(g, 0.0)
+        return r * r * u
+    if act_fn == "swiglu_oai":
+        gc = np.minimum(g, OAI_LIMIT)
+        uc = np.clip(u, -OAI_LIMIT, OAI_LIMIT)
+        with np.errstate(over="ignore"):
+            return (uc + 1.0) * (gc / (1.0 + np.exp(-OAI_ALPHA * gc)))
+    raise ValueError(act_fn)
+
+
 def decode_weight(packed: np.ndarray, scales: np.ndarray, fmt: str, k: int) -> np.ndarray:
     """One expert's packed weight [N, k*bits/8] + scales [N, k/32] -> float64 [N, k]."""
     codes = mx.unpack(packed, fmt, k)
@@ -80,31 +107,32 @@ def intermediate(h: np.ndarray, act: str) -> np.ndarray:
     raise ValueError(act)
 
 
-def expert_hidden(a: np.ndarray, w1: np.ndarray) -> np.ndarray:
-    """a [M, H] float64, decoded w1 [2I, H] -> h = SiLU(gate) * up [M, I] (FC1
+def expert_hidden(a: np.ndarray, w1: np.ndarray, act_fn: str = "silu") -> np.ndarray:
+    """a [M, H] float64, decoded w1 [2I, H] -> h = act(gate, up) [M, I] (FC1
     and the gated activation, before the intermediate rounding)."""
     I = w1.shape[0] // 2
     z = a @ w1.T                      # FC1, K = H
     g, u = z[:, :I], z[:, I:]
-    return silu(g) * u
+    return gated(g, u, act_fn)
 
 
-def expert_ffn(a: np.ndarray, w1: np.ndarray, w2: np.ndarray, act: str) -> np.ndarray:
+def expert_ffn(a: np.ndarray, w1: np.ndarray, w2: np.ndarray, act: str, act_fn: str = "silu") -> np.ndarray:
     """a [M, H] float64, decoded w1 [2I, H], decoded w2 [H, I] -> o [M, H]."""
-    ht = intermediate(expert_hidden(a, w1), act)
+    ht = intermediate(expert_hidden(a, w1, act_fn), act)
     return ht @ w2.T                  # FC2, K = I
 
 
 def moe_forward(x, logits, w1, w1_scale, w2, w2_scale, *, k, wfmt, act,
                 topk_ids=None, topk_w=None,
                 shared=None, shared_weight=1.0,
-                local_offset=0, local_count=None, tokens=None, intermediates=False):
+                local_offset=0, local_count=None, tokens=None, intermediates=False, act_fn="silu"):
     """Full layer output in float64.
 
     x [T, H] exact bf16 values (float64); logits [T, E] float32 (or None when
     topk_ids / topk_w are given); w1 [E, 2I, H*b/8] uint8 + w1_scale [E, 2I, H/32];
     w2 [E, H, I*b/8] + w2_scale [E, H, I/32]; wfmt "e2m1" | "e3m2";
-    act "bf16" | "mxfp8"; shared = (ws1, ws1_scale, ws2, ws2_scale) or None.
+    act "bf16" | "mxfp8"; shared = (ws1, ws1_scale, ws2, ws2_scale) or None;
+    act_fn the gated activation of every expert ("silu", "relu2", "swiglu_oai").
     ``tokens`` restricts the computation to a subset of token rows (each
     token's output depends only on its own row); the result then has one row
     per listed token.
@@ -144,7 +172,7 @@ def moe_forward(x, logits, w1, w1_scale, w2, w2_scale, *, k, wfmt, act,
         d1 = decode_weight(w1[e], w1_scale[e], wfmt, H)
         d2 = decode_weight(w2[e], w2_scale[e], wfmt, I)
         if intermediates:
-            h = expert_hidden(a[t_loc], d1)
+            h = expert_hidden(a[t_loc], d1, act_fn)
             if act == "mxfp8":
                 codes, scales = mx.quantize(h, "e4m3")
                 for r, asg in enumerate(seg):
@@ -152,14 +180,14 @@ def moe_forward(x, logits, w1, w1_scale, w2, w2_scale, *, k, wfmt, act,
             else:
                 for r, asg in enumerate(seg):
                     inter[int(asg)] = intermediate(h[r:r + 1], act)[0]
-        o = expert_ffn(a[t_loc], d1, d2, act)
+        o = expert_ffn(a[t_loc], d1, d2, act, act_fn)
         y[t_loc] += w[t_loc, slot][:, None] * o   # a token meets an expert at most once
     if shared is not None:
         ws1, ws1_scale, ws2, ws2_scale = shared
         Is = ws1.shape[0] // 2
         d1 = decode_weight(ws1, ws1_scale, wfmt, H)
         d2 = decode_weight(ws2, ws2_scale, wfmt, Is)
-        y += shared_weight * expert_ffn(a, d1, d2, act)
+        y += shared_weight * expert_ffn(a, d1, d2, act, act_fn)
     out = dict(y=y, ids=ids, w=w, counts=counts, offsets=offsets, sorted_assign=sorted_assign)
     if intermediates:
         out["intermediates"] = inter

@@ -234,3 +234,51 @@ def test_silu_closed_forms():
     s = om.silu(g)
     assert s[0] == 0.0 and abs(s[1] - 50.0) < 1e-15 * 50 and abs(s[2]) < 1e-19
     assert abs(s[3] - 1.0 / (1.0 + np.exp(-1.0))) < 1e-16 and s[4] == 0.0
+
+
+def test_gated_activation_closed_forms():
+    """Values worked by hand at points where each form is elementary."""
+    g = np.array([0.0, 2.0, -3.0, 1.0, 7.0, 10.0, -0.5])
+    u = np.array([5.0, 3.0, 4.0, -10.0, 0.0, 2.0, 9.0])
+    # SiLU: g / (1 + e^-g) * u
+    s = om.gated(g, u, "silu")
+    assert s[0] == 0.0 and abs(s[1] - 2.0 / (1 + np.exp(-2.0)) * 3.0) < 1e-15
+    # ReLU2: relu(g)^2 * u -> 0, 12, 0, -10, 0, 200, 0
+    r = om.gated(g, u, "relu2")
+    assert np.array_equal(r, np.array([0.0, 12.0, 0.0, -10.0, 0.0, 200.0, 0.0]))
+    # SwiGLU-OAI: gate clipped above at 7, up clipped to [-7, 7], (u + 1) * g sigmoid(1.702 g)
+    o = om.gated(g, u, "swiglu_oai")
+    sig = lambda z: 1.0 / (1.0 + np.exp(-z))  # noqa: E731
+    assert o[0] == 0.0                                   # g = 0
+    assert abs(o[1] - 4.0 * 2.0 * sig(3.404)) < 1e-14    # (3 + 1) * 2 * sig(1.702 * 2)
+    assert abs(o[3] - (-6.0) * 1.0 * sig(1.702)) < 1e-14  # up clipped to -7: (-7 + 1)
+    assert abs(o[4] - 1.0 * 7.0 * sig(11.914)) < 1e-14   # (0 + 1) * 7 * sig(1.702 * 7)
+    assert o[5] == 3.0 * 7.0 * sig(11.914)               # gate clipped from 10 to 7
+    assert o[6] < 0 and abs(o[6] - 8.0 * -0.5 * sig(-0.851)) < 1e-14   # up 9 clipped to 7
+    # the gate is clipped from above only: g = -10 stays -10
+    assert om.gated(np.array([-10.0]), np.array([1.0]), "swiglu_oai")[0] == 2.0 * -10.0 * sig(-17.02)
+    with pytest.raises(ValueError):
+        om.gated(g, u, "gelu")
+
+
+@pytest.mark.parametrize("act_fn", ["relu2", "swiglu_oai"])
+def test_activation_variant_reaches_every_expert(act_fn):
+    """The chosen activation replaces SiLU in every routed and shared expert:
+    with identical experts the layer is the dense MLP with that activation."""
+    rng = np.random.default_rng(15)
+    p1, s1, p2, s2 = _weights(rng, 1, I, H, "e2m1", std=0.1)
+    P1, S1, P2, S2 = (np.repeat(a, E, axis=0) for a in (p1, s1, p2, s2))
+    x = _x(rng, T, H)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    d1 = om.decode_weight(p1[0], s1[0], "e2m1", H)
+    d2 = om.decode_weight(p2[0], s2[0], "e2m1", I)
+    z = x @ d1.T
+    h = mx.round_to_bf16(om.gated(z[:, :I], z[:, I:], act_fn))
+    ref = h @ d2.T
+    y = om.moe_forward(x, lg, P1, S1, P2, S2, k=2, wfmt="e2m1", act="bf16", act_fn=act_fn)["y"]
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-14)
+    ys = om.moe_forward(x, lg, P1, S1, P2, S2, k=2, wfmt="e2m1", act="bf16", act_fn=act_fn,
+                        shared=(p1[0], s1[0], p2[0], s2[0]), shared_weight=0.5)["y"]
+    assert np.allclose(ys, 1.5 * ref, rtol=1e-12, atol=1e-14)
+    silu = om.moe_forward(x, lg, P1, S1, P2, S2, k=2, wfmt="e2m1", act="bf16")["y"]
+    assert not np.allclose(silu, y)
