@@ -304,6 +304,33 @@ static moe_status_t validate(const moe_problem_t* p, const moe_tensors_t* t) {
   return MOE_OK;
 }
 
+// ----------------------------------------------------- no-alloc scratch ----
+
+// Workspace of moe_fused_noalloc: one array per device that loads the
+// library, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, so its device address is looked up once per device
+// (scratch_ptr) and only that address is passed to kernels.
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call per device (nullptr if the lookup fails).
+static void* scratch_ptr(moe_status_t* st) {
+  static std::atomic<void*> ptrs[256];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) {
+    *st = MOE_ERR_ARCH;
+    return nullptr;
+  }
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+    *st = MOE_ERR_HIP;
+    return nullptr;
+  }
+  ptrs[dev].store(p, std::memory_order_release);  // the same address however many threads race here
+  return p;
+}
+
 }  // namespace moe_mx
 
 using namespace moe_mx;
@@ -646,4 +673,17 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   if (!ok(hipGetLastError())) return MOE_ERR_HIP;
   if (!mark(MOE_NUM_STAGES)) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+extern "C" moe_status_t moe_fused_noalloc(const moe_problem_t* p, const moe_tensors_t* t, hipStream_t stream) {
+  moe_status_t v = validate(p, t);
+  if (v != MOE_OK) return v;
+  if (p->T == 0) return MOE_OK;
+  if (plan(*p).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  moe_status_t a = check_arch();
+  if (a != MOE_OK) return a;
+  moe_status_t st = MOE_OK;
+  void* ws = scratch_ptr(&st);
+  if (!ws) return st;
+  return moe_fused(p, t, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }

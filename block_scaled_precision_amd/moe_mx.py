@@ -23,8 +23,9 @@ ACTS = {"bf16": 0, "mxfp8": 1}
 
 # Every symbol include/moe_mx.h declares.
 EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "mx_gemm_workspace_bytes", "mx_gemm",
-           "moe_fused_workspace_bytes", "moe_fused", "moe_fused_workspace_offset", "moe_status_str",
-           "moe_mx_version")
+           "moe_fused_workspace_bytes", "moe_fused", "moe_fused_workspace_offset", "moe_fused_noalloc",
+           "moe_status_str", "moe_mx_version")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -76,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp,
                               sz, vp]
         L.mx_gemm.restype = ctypes.c_int
+        L.moe_fused_noalloc.argtypes = [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeTensors), vp]
+        L.moe_fused_noalloc.restype = ctypes.c_int
         L.moe_fused_workspace_offset.argtypes = [ctypes.POINTER(MoeProblem), ctypes.c_int]
         L.moe_fused_workspace_offset.restype = sz
         L.moe_status_str.argtypes = [ctypes.c_int]
@@ -330,7 +333,8 @@ def check_fused_args(problem: MoeProblem, x, weights, router_logits=None, topk_i
         _require(topk_ids_out, "topk_ids_out", torch.int32, (T, k))
     if topk_w_out is not None:
         _require(topk_w_out, "topk_w_out", torch.float32, (T, k))
-    _require_workspace(workspace, moe_fused_workspace_bytes(p))
+    if workspace is not None:
+        _require_workspace(workspace, moe_fused_workspace_bytes(p))
     _dev(x, y, router_logits, topk_ids_in, topk_w_in, weights.w1, weights.w1_scale, weights.w2,
          weights.w2_scale, *shared, topk_ids_out, topk_w_out, workspace)
 
@@ -357,6 +361,22 @@ def moe_fused(problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, router_
         t.stage_events = ctypes.cast(stage_events, ctypes.c_void_p)
     _check(lib().moe_fused(ctypes.byref(problem), ctypes.byref(t), _ptr(workspace), workspace.numel(),
                            _stream(stream)), "moe_fused")
+    return y
+
+
+def moe_fused_noalloc(problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, y: torch.Tensor,
+                      router_logits=None, topk_ids_in=None, topk_w_in=None, topk_ids_out=None,
+                      topk_w_out=None, stream=None):
+    """The whole layer into the caller's y, with the library's static scratch
+    as workspace: nothing is allocated (y must be given)."""
+    if problem.T > 0:
+        check_fused_args(problem, x, weights, router_logits, topk_ids_in, topk_w_in, y, None,
+                         topk_ids_out, topk_w_out)
+    t = MoeTensors(*(None if v is None else v.data_ptr() for v in (
+        x, router_logits, topk_ids_in, topk_w_in, weights.w1, weights.w1_scale, weights.w2,
+        weights.w2_scale, weights.ws1, weights.ws1_scale, weights.ws2, weights.ws2_scale, y,
+        topk_ids_out, topk_w_out)), None)
+    _check(lib().moe_fused_noalloc(ctypes.byref(problem), ctypes.byref(t), _stream(stream)), "moe_fused_noalloc")
     return y
 
 

@@ -255,6 +255,24 @@ typedef enum {
 } moe_ws_part_t;
 size_t moe_fused_workspace_offset(const moe_problem_t* p, moe_ws_part_t part);
 
+/*
+ * moe_fused_noalloc -- moe_fused for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same problem, tensors and results as moe_fused,
+ * without a workspace argument.  Its workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that every device using the library holds until
+ * the process ends; the call itself allocates nothing.
+ *   - A problem whose moe_fused_workspace_bytes() exceeds the array returns
+ *     MOE_ERR_WORKSPACE (e.g. T = 64 at H = 7168, I = 2048, k = 8 needs about
+ *     10 MiB).
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's contents (nothing in it needs to start at zero): calls that
+ *     overlap on one device (other streams, other threads) race and must be
+ *     serialised by the caller.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status_t moe_fused_noalloc(const moe_problem_t* p, const moe_tensors_t* t, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_str(moe_status_t s);
 
