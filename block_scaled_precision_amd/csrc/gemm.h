@@ -31,6 +31,7 @@ struct FcArgs {
   const uint8_t* w_scale;
   int64_t w_estride;   // bytes per expert
   int64_t ws_estride;  // scale bytes per expert
+  int act_fn;          // FC1: gated activation (moe_act_fn_t; 0 = SiLU)
   int K;               // contraction length (H for FC1, I for FC2)
   int N;               // FC1: I (h columns); FC2: H
   int nchunks;         // column chunks of N per M-tile

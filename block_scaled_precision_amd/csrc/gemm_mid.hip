@@ -225,7 +225,7 @@ __device__ __forceinline__ void mid_multiply(const FcArgs& p, const MSched& sc, 
             if (row < it.rows) {
               uint16_t* o = out + (int64_t)(it.p0 + row) * p.N + it.nb * (MBN / 2) + 64 * wc + r16;
 #pragma unroll
-              for (int n = 0; n < 4; ++n) o[16 * n] = f32_to_bf16_rne(silu_mul(acc[m][n][i], acc[m][n + 4][i]));
+              for (int n = 0; n < 4; ++n) o[16 * n] = f32_to_bf16_rne(gated_act(p.act_fn, acc[m][n][i], acc[m][n + 4][i]));
             }
           }
       } else {

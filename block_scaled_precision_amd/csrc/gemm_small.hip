@@ -201,7 +201,7 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * g + i;
-        if (row < it.rows) out[(int64_t)(it.p0 + row) * p.N + col] = f32_to_bf16_rne(silu_mul(acc[0][i], acc[1][i]));
+        if (row < it.rows) out[(int64_t)(it.p0 + row) * p.N + col] = f32_to_bf16_rne(gated_act(p.act_fn, acc[0][i], acc[1][i]));
       }
     } else {
       int orow[4];

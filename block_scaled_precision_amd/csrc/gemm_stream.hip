@@ -19,7 +19,7 @@
 //    [64+16g, +16); lane l's scale byte applies to (row l%16, k block l/16).
 //
 // bf16 activations: weights are dequantized in registers with
-// v_cvt_scalef32_pk_bf16_fp4 (E2M1) or v_cvt_scalef32_pk32_bf16_fp6 (E3M2),
+// v_cvt_scalef32_pk_bf16_fp4 (E2M1) or v_cvt_scalef32_pk32_bf16_bf6 (E3M2, the "bf6" format),
 // exact for E8M0 scales, and multiplied on the bf16 MFMA.  MXFP8 activations: codes and scales feed the scaled MFMA
 // directly (TokenSpeed SiTU page, "Activation precision": MXFP8 activation x
 // MXFP4 weight; mxfp6-sm120 page: block-scaled MMA with FP32 accumulation).
@@ -99,7 +99,7 @@ __device__ __forceinline__ void mma_chunk(v4f (&acc)[NB], const AFrag& a, const 
       const float sc = e8m0_to_f32((b[n].scale >> (8 * g)) & 0xffu);
       const v6i src = {(int)b[n].d[0], (int)b[n].d[1], (int)b[n].d[2], (int)b[n].d[3], (int)b[n].d[4],
                        (int)b[n].d[5]};
-      const v32bf wv = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(src, sc);
+      const v32bf wv = __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(src, sc);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const v8bf bv = {wv[8 * s], wv[8 * s + 1], wv[8 * s + 2], wv[8 * s + 3],
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hv[h][i] = silu_mul(acc[h][i], acc[h + 2][i]);
+    for (int i = 0; i < 4; ++i) hv[h][i] = gated_act(p.act_fn, acc[h][i], acc[h + 2][i]);
   if (!MXA) {
     uint16_t* out = (uint16_t*)p.out;
 #pragma unroll

@@ -337,7 +337,7 @@ __device__ __forceinline__ void multiply_role(const FcArgs& p, const Sched& sc, 
         if (FC1) {
           // h = SiLU(gate) * up for column nb*64 + 32*wn + l32, then one E4M3
           // block per (row, 32 columns) with its E8M0 scale
-          const float h = silu_mul(acc[m][0][i], acc[m][1][i]);
+          const float h = gated_act(p.act_fn, acc[m][0][i], acc[m][1][i]);
           uint32_t mx = __float_as_uint(h) & 0x7fffffffu;
 #pragma unroll
           for (int off = 1; off < 32; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));

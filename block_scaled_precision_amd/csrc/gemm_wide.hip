@@ -405,6 +405,10 @@ struct BCopier {
 __device__ __forceinline__ float silu_mul_fast(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504f)) * u;
 }
+// the gated activation: SiLU as above, the other forms as everywhere else
+__device__ __forceinline__ float act_mul(int fn, float g, float u) {
+  return fn == MOE_FN_SILU ? silu_mul_fast(g, u) : gated_act(fn, g, u);
+}
 
 // Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
 __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
@@ -561,8 +565,8 @@ __device__ __forceinline__ void wave_main(const FcArgs& p, const Sched& sc, uint
           // lanes of a row are one DPP row.
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            const float h0 = silu_mul_fast(acc[m][2 * b][i], acc[m][2 * b + 4][i]);
-            const float h1 = silu_mul_fast(acc[m][2 * b + 1][i], acc[m][2 * b + 5][i]);
+            const float h0 = act_mul(p.act_fn, acc[m][2 * b][i], acc[m][2 * b + 4][i]);
+            const float h1 = act_mul(p.act_fn, acc[m][2 * b + 1][i], acc[m][2 * b + 5][i]);
             const uint32_t mx = row16_max(max(__float_as_uint(h0) & 0x7fffffffu, __float_as_uint(h1) & 0x7fffffffu));
             const int sexp = block_exponent<3>(mx);
             const uint32_t codes = e4m3_pair(h0 * exp2_neg(sexp), h1 * exp2_neg(sexp));

@@ -279,6 +279,8 @@ static moe_status_t validate(const moe_problem_t* p, const moe_tensors_t* t) {
   if (p->E < 1 || p->E > kMaxExperts || p->k < 1 || p->k > p->E) return MOE_ERR_INVALID_ARG;
   if (p->w_fmt != MX_E2M1 && p->w_fmt != MX_E3M2 && p->w_fmt != MX_E4M3) return MOE_ERR_INVALID_ARG;
   if (p->act != MOE_ACT_BF16 && p->act != MOE_ACT_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (p->act_fn != MOE_FN_SILU && p->act_fn != MOE_FN_RELU2 && p->act_fn != MOE_FN_SWIGLU_OAI)
+    return MOE_ERR_INVALID_ARG;
   const int L = p->local_num_experts == 0 ? p->E : p->local_num_experts;
   if (p->local_expert_offset < 0 || L < 0 || (int64_t)p->local_expert_offset + L > p->E)
     return MOE_ERR_INVALID_ARG;
@@ -457,11 +459,11 @@ extern "C" moe_status_t mx_gemm(const void* a, const uint8_t* a_scale, int64_t M
       return MOE_ERR_INVALID_ARG;
   }
   if (w_fmt == MX_E4M3 || N % 8 || K % 128) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
   const bool quant = act == MOE_ACT_MXFP8 && !a_scale;
   const size_t need = quant ? mx_gemm_workspace_bytes(M, K, act) : 0;
   if (quant && (workspace_bytes < need || !workspace)) return MOE_ERR_WORKSPACE;
   if (quant && ((uintptr_t)workspace & 255u) != 0) return MOE_ERR_INVALID_ARG;
-  if (M == 0) return MOE_OK;
   moe_status_t st = check_arch();
   if (st != MOE_OK) return st;
 
@@ -601,6 +603,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   a1.w_scale = t->w1_scale;
   a1.w_estride = 2 * (int64_t)I * bytes_h;
   a1.ws_estride = 2 * (int64_t)I * (H / 32);
+  a1.act_fn = p->act_fn;
   a1.K = H;
   a1.N = I;
   a1.nchunks = I / fc_cols(f.routed, true, f.bm);

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_mx.h"
+
 namespace moe_mx {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -94,5 +96,26 @@ __device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
 
 // SiLU(g) * u in fp32.
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Gated activations of FC1's two halves (b12x page, "What's in here", MoE:
+// SiLU, ReLU2 and SwiGLU-OAI), in fp32; `fn` is a moe_act_fn_t value and is
+// uniform across a launch.
+//   SiLU        SiLU(g) * u
+//   ReLU2       max(g, 0)^2 * u
+//   SwiGLU-OAI  (clamp(u, -7, 7) + 1) * g' * sigmoid(1.702 g'), g' = min(g, 7)
+constexpr float kOaiLimit = 7.0f;
+constexpr float kOaiAlpha = 1.702f;
+__device__ __forceinline__ float gated_act(int fn, float g, float u) {
+  if (fn == MOE_FN_RELU2) {
+    const float r = fmaxf(g, 0.0f);
+    return r * r * u;
+  }
+  if (fn == MOE_FN_SWIGLU_OAI) {
+    const float gc = fminf(g, kOaiLimit);
+    const float uc = fminf(fmaxf(u, -kOaiLimit), kOaiLimit);
+    return (uc + 1.0f) * (gc / (1.0f + expf(-kOaiAlpha * gc)));
+  }
+  return silu_mul(g, u);
+}
 
 }  // namespace moe_mx

@@ -20,6 +20,7 @@ MX_FORMATS = {"e2m1": 1, "e3m2": 2, "e4m3": 3}
 FORMAT_BITS = {"e2m1": 4, "e3m2": 6, "e4m3": 8}
 SRC_DTYPES = {torch.bfloat16: 0, torch.float32: 1}
 ACTS = {"bf16": 0, "mxfp8": 1}
+ACT_FNS = {"silu": 0, "relu2": 1, "swiglu_oai": 2}
 
 # Every symbol include/moe_mx.h declares.
 EXPORTS = ("mx_quantize", "moe_route_workspace_bytes", "moe_route", "mx_gemm_workspace_bytes", "mx_gemm",
@@ -38,7 +39,8 @@ class MoeProblem(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("w_fmt", ctypes.c_int),
                 ("act", ctypes.c_int), ("I_shared", ctypes.c_int32), ("shared_weight", ctypes.c_float),
-                ("local_expert_offset", ctypes.c_int32), ("local_num_experts", ctypes.c_int32)]
+                ("local_expert_offset", ctypes.c_int32), ("local_num_experts", ctypes.c_int32),
+                ("act_fn", ctypes.c_int)]
 
 
 MOE_NUM_STAGES = 7
@@ -267,9 +269,10 @@ class MoeWeights:
     ws2_scale: torch.Tensor | None = None
 
 
-def make_problem(T, H, I, E, k, fmt, act, I_shared=0, shared_weight=1.0, local_offset=0, local_count=0):
+def make_problem(T, H, I, E, k, fmt, act, I_shared=0, shared_weight=1.0, local_offset=0, local_count=0,
+                 act_fn="silu"):
     return MoeProblem(T, H, I, E, k, MX_FORMATS[fmt], ACTS[act], I_shared, shared_weight,
-                      local_offset, local_count)
+                      local_offset, local_count, ACT_FNS[act_fn])
 
 
 def moe_fused_workspace_bytes(problem: MoeProblem) -> int:

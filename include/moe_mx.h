@@ -11,8 +11,9 @@
  *      scale per 32 hidden values;
  *   4. FC1: gathered rows times W1 = [gate; up] (MXFP4 E2M1 or MXFP6 E3M2,
  *      one E8M0 scale per 32 along K), fp32 accumulation;
- *   5. h = SiLU(gate) * up in fp32, stored as bf16 (bf16 activations) or
- *      requantized to MXFP8 along I (MXFP8 activations);
+ *   5. h = SiLU(gate) * up (or another gated activation, act_fn) in fp32,
+ *      stored as bf16 (bf16 activations) or requantized to MXFP8 along I
+ *      (MXFP8 activations);
  *   6. FC2: h times W2, fp32 accumulation;
  *   7. y[t] = sum_j w[t,j] * FC2 output of (t, j), plus an optional shared
  *      expert with its own weight: each weighted expert row is rounded to
@@ -78,6 +79,14 @@ typedef enum { MOE_SRC_BF16 = 0, MOE_SRC_FP32 = 1 } moe_src_t;
  * precision"): bf16 activations (w4a16) or MXFP8 E4M3 activations (w4a8 /
  * w6a8) quantized on the device. */
 typedef enum { MOE_ACT_BF16 = 0, MOE_ACT_MXFP8 = 1 } moe_act_t;
+
+/* Gated activation applied to FC1's gate half g and up half u (b12x page,
+ * "What's in here", MoE: SiLU, ReLU2 and SwiGLU-OAI activations), in fp32:
+ *   MOE_FN_SILU        SiLU(g) * u = g / (1 + exp(-g)) * u   (default)
+ *   MOE_FN_RELU2       max(g, 0)^2 * u
+ *   MOE_FN_SWIGLU_OAI  (clamp(u, -7, 7) + 1) * g' / (1 + exp(-1.702 g')),
+ *                      g' = min(g, 7)  (the gpt-oss form) */
+typedef enum { MOE_FN_SILU = 0, MOE_FN_RELU2 = 1, MOE_FN_SWIGLU_OAI = 2 } moe_act_fn_t;
 
 /*
  * mx_quantize -- block quantization of a row-major matrix to MX codes.
@@ -171,6 +180,7 @@ typedef struct {
   float shared_weight;         /* weight of the shared expert's output (e.g. 1.0)    */
   int32_t local_expert_offset; /* first expert held by this call (TokenSpeed SiTU    */
   int32_t local_num_experts;   /* page, "Supported contract"); 0 means all E         */
+  moe_act_fn_t act_fn;         /* gated activation of every expert (0 = SiLU)       */
 } moe_problem_t;
 
 /* Tensors of one call.  W1/W2 hold only the local experts: expert index

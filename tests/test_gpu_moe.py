@@ -162,6 +162,22 @@ def test_shared_weight(name, sw):
     assert_y_close(y.float().cpu().numpy(), ref["y"], f"{name} shared_weight={sw}")
 
 
+# the gated activations (b12x page, "What's in here", MoE) through each kernel
+# family's FC1 epilogue: small-M, mid-M, tiled (+ shared), wide, stream
+@pytest.mark.parametrize("act_fn", ["relu2", "swiglu_oai"])
+@pytest.mark.parametrize("name", ["w4a16_small_gs4", "skew_w4a16_mid", "w6a8_shared_small",
+                                  "w4a8_wide_multi_tile", "w4a8_h384", "w6a16_shared"])
+def test_activation_variants(name, act_fn):
+    w, gw, arrs, shared, x, logits, m = _prepare(name)
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared, act_fn=act_fn)
+    print_flush(f"moe_fused {name} act_fn={act_fn}")
+    y = m.moe_fused(prob, x.cuda(), gw, router_logits=logits.cuda())
+    torch.cuda.synchronize()
+    ref = _oracle_y(w, arrs, shared, x, logits, act_fn=act_fn)
+    mr, rr = assert_y_close(y.float().cpu().numpy(), ref["y"], f"{name} {act_fn}")
+    print_flush(f"  max_rel={mr:.2e} rms_rel={rr:.2e}")
+
+
 def _wide_schedule_parts(counts, nb, grid=256):
     """For the wide kernel's persistent schedule on `grid` workgroups: number of
     tiles, whole tiles per XCD, and whether some workgroup streams an item of
@@ -229,14 +245,18 @@ def test_intermediate_flip_rate(name):
         print_flush(f"  {name}: E4M3 code flips {code_flips:.2e}, E8M0 scale flips {scale_flips:.2e}")
         # a flip is a value on the other side of one rounding boundary: the
         # block scales differ by at most one step, and each decoded value by
-        # at most one E4M3 step (1/8 of the larger magnitude, or the
-        # subnormal step 2**-9 times the block scale)
-        from oracle.mx import decode_e8m0, dequantize
+        # one E4M3 step (1/8 of the larger magnitude) plus what fp32
+        # accumulation error can reach near zero (2**-12 of the block's
+        # largest value); a misplaced or wrong value would be off by O(1)
+        # of the block maximum
+        from oracle.mx import dequantize
         assert np.abs(scales.astype(int) - osc.astype(int)).max() <= 1
         gv, ov = dequantize(codes, scales, "e4m3"), dequantize(oc, osc, "e4m3")
-        step = np.maximum(np.abs(gv), np.abs(ov)) / 8 + np.repeat(
-            np.maximum(decode_e8m0(scales), decode_e8m0(osc)), 32, axis=1) * 2.0 ** -9
-        assert np.all(np.abs(gv - ov) <= step)
+        bmax = np.repeat(np.abs(ov).reshape(A, -1, 32).max(axis=2), 32, axis=1)
+        tol = np.maximum(np.abs(gv), np.abs(ov)) / 8 + bmax * 2.0 ** -12
+        worst = float(np.max(np.abs(gv - ov) / np.where(tol > 0, tol, 1.0)))
+        print_flush(f"  largest difference / (one step + 2**-12 block max): {worst:.3f}")
+        assert worst <= 1.0
         assert code_flips <= 5e-3 and scale_flips <= 5e-3
     else:
         h = part("h", A * w.I * 2).view(np.uint16).reshape(A, w.I)
@@ -245,8 +265,13 @@ def test_intermediate_flip_rate(name):
         want = np.stack([inter[int(a)] for a in sa])
         flips = float(np.mean(got != want))
         print_flush(f"  {name}: bf16 intermediate flips {flips:.2e}")
-        # each flip is one bf16 step (8 significant bits)
-        assert np.all(np.abs(got - want) <= np.maximum(np.abs(got), np.abs(want)) * 2.0 ** -7)
+        # each flip is one bf16 step (8 significant bits) plus what fp32
+        # accumulation error can reach near zero (2**-14 of the row maximum)
+        rmax = np.abs(want).max(axis=1, keepdims=True)
+        tol = np.maximum(np.abs(got), np.abs(want)) * 2.0 ** -7 + rmax * 2.0 ** -14
+        worst = float(np.max(np.abs(got - want) / np.where(tol > 0, tol, 1.0)))
+        print_flush(f"  largest difference / (one step + 2**-14 row max): {worst:.3f}")
+        assert worst <= 1.0
         assert flips <= 5e-3
 
 
