@@ -54,7 +54,7 @@ BOUND = {
 FC1_KERNEL = {
     "tiny_w4a16": "k_fc_small<true, 1>",
     "decode_w4a16": "k_fc_small<true, 4>",
-    "prefill_w4a8": "k_fc_wide<true>",
+    "prefill_w4a8": "k_fc_wide<true, 0>",
     "skew_w4a16": "k_fc_mid<true, 128>",
     "w6a8_shared": "k_fc_tiled<true, 2, 128, false>",
 }

@@ -405,9 +405,12 @@ struct BCopier {
 __device__ __forceinline__ float silu_mul_fast(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504f)) * u;
 }
-// the gated activation: SiLU as above, the other forms as everywhere else
-__device__ __forceinline__ float act_mul(int fn, float g, float u) {
-  return fn == MOE_FN_SILU ? silu_mul_fast(g, u) : gated_act(fn, g, u);
+// the gated activation, fixed per instantiation (a run-time choice in this
+// epilogue made the compiler spill registers in the step loop): SiLU as
+// above, the other forms as in every other kernel
+template <int ACT>
+__device__ __forceinline__ float act_mul(float g, float u) {
+  return ACT == MOE_FN_SILU ? silu_mul_fast(g, u) : gated_act(ACT, g, u);
 }
 
 // Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
@@ -510,7 +513,7 @@ __device__ __forceinline__ void item_steps(const FcArgs& p, const Sched& sc, v4f
   }
 }
 
-template <bool FC1, class Copier>
+template <bool FC1, int ACT, class Copier>
 __device__ __forceinline__ void wave_main(const FcArgs& p, const Sched& sc, uint8_t* smem, int wm, int wn) {
   const int lane = threadIdx.x & 63;
   const int l16 = lane & 15, g = lane >> 4;
@@ -565,8 +568,8 @@ __device__ __forceinline__ void wave_main(const FcArgs& p, const Sched& sc, uint
           // lanes of a row are one DPP row.
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            const float h0 = act_mul(p.act_fn, acc[m][2 * b][i], acc[m][2 * b + 4][i]);
-            const float h1 = act_mul(p.act_fn, acc[m][2 * b + 1][i], acc[m][2 * b + 5][i]);
+            const float h0 = act_mul<ACT>(acc[m][2 * b][i], acc[m][2 * b + 4][i]);
+            const float h1 = act_mul<ACT>(acc[m][2 * b + 1][i], acc[m][2 * b + 5][i]);
             const uint32_t mx = row16_max(max(__float_as_uint(h0) & 0x7fffffffu, __float_as_uint(h1) & 0x7fffffffu));
             const int sexp = block_exponent<3>(mx);
             const uint32_t codes = e4m3_pair(h0 * exp2_neg(sexp), h1 * exp2_neg(sexp));
@@ -609,7 +612,7 @@ __device__ __forceinline__ void wave_main(const FcArgs& p, const Sched& sc, uint
   wait_vm_lgkm0<0>();
 }
 
-template <bool FC1>
+template <bool FC1, int ACT>
 __global__ __launch_bounds__(kThreads, 1) void k_fc_wide(FcArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L_TOTAL];
   Sched sc;
@@ -629,8 +632,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_fc_wide(FcArgs p) {
   // the wave index is uniform; saying so keeps everything derived from it
   // (copy cursors, sub-block counts, branches) in scalar registers
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w < 4) wave_main<FC1, ACopier<FC1>>(p, sc, smem, w, 0);
-  else wave_main<FC1, BCopier<FC1>>(p, sc, smem, w - 4, 1);
+  if (w < 4) wave_main<FC1, ACT, ACopier<FC1>>(p, sc, smem, w, 0);
+  else wave_main<FC1, ACT, BCopier<FC1>>(p, sc, smem, w - 4, 1);
 }
 
 }  // namespace
@@ -638,8 +641,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_fc_wide(FcArgs p) {
 hipError_t launch_fc_wide(const FcArgs& p, bool fc1, int grid, hipStream_t st) {
   if (grid < 8) grid = 8;
   grid &= ~7;
-  if (fc1) k_fc_wide<true><<<grid, kThreads, 0, st>>>(p);
-  else k_fc_wide<false><<<grid, kThreads, 0, st>>>(p);
+  if (!fc1) k_fc_wide<false, MOE_FN_SILU><<<grid, kThreads, 0, st>>>(p);
+  else if (p.act_fn == MOE_FN_RELU2) k_fc_wide<true, MOE_FN_RELU2><<<grid, kThreads, 0, st>>>(p);
+  else if (p.act_fn == MOE_FN_SWIGLU_OAI) k_fc_wide<true, MOE_FN_SWIGLU_OAI><<<grid, kThreads, 0, st>>>(p);
+  else k_fc_wide<true, MOE_FN_SILU><<<grid, kThreads, 0, st>>>(p);
   return hipGetLastError();
 }
 
