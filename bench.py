@@ -280,28 +280,35 @@ def event_median(torch, m, fn, steps, warmup):
 
 def small_batches(torch, np, m, gen, mw, args, batches=(1, 2, 4, 8)):
     """The decode shapes (H=7168, I=2048, E=384 resident experts, top-8, bf16
-    activations) at batches of 1 to 8 tokens: the whole layer per call, and
-    the packed weights of the experts the batch routes to (what the call must
-    stream from HBM) per second against the HBM peak."""
+    activations) at batches of 1 to 8 tokens, on the default path and on the
+    fused small-batch path: the whole layer per call, and the packed weights
+    of the experts the batch routes to (what the call must stream from HBM)
+    per second against the HBM peak."""
     base = gen.WORKLOADS[HEADLINE]
     out = {}
     for T in batches:
         w = gen.scaled(base, T=T)
         logits = gen.router_logits(w, args.seed, device="cuda")
         x = gen.hidden_states(w, args.seed, device="cuda")
-        prob = m.make_problem(T, w.H, w.I, w.E, w.k, w.wfmt, w.act)
-        ws = torch.empty((m.moe_fused_workspace_bytes(prob),), dtype=torch.uint8, device="cuda")
         y = torch.empty((T, w.H), dtype=torch.bfloat16, device="cuda")
         ids = torch.empty((T, w.k), dtype=torch.int32, device="cuda")
-        fn = lambda: m.moe_fused(prob, x, mw, router_logits=logits, y=y, workspace=ws, topk_ids_out=ids)  # noqa: E731
-        ms = event_median(torch, m, fn, args.steps, args.warmup)
-        counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
-        work = algorithmic_work(w, counts)
-        wbytes = work["active_experts"] * (work["per_expert_w1_bytes"] + work["per_expert_w2_bytes"])
-        gbs = wbytes / (ms / 1e3) / 1e9
-        out[str(T)] = {"ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "active_experts": work["active_experts"],
-                       "weight_bytes": wbytes, "weight_GB_per_s": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
-        log(f"# decode shapes T={T}: {ms * 1e3:.1f} us, {work['active_experts']} experts, {gbs:.0f} GB/s of weights")
+        row = {}
+        for path, fused in (("default", False), ("fused_small_batch", True)):
+            prob = m.make_problem(T, w.H, w.I, w.E, w.k, w.wfmt, w.act, fused_small_batch=fused)
+            ws = torch.empty((m.moe_fused_workspace_bytes(prob),), dtype=torch.uint8, device="cuda")
+            fn = lambda: m.moe_fused(prob, x, mw, router_logits=logits, y=y, workspace=ws,  # noqa: E731
+                                     topk_ids_out=ids)
+            ms = event_median(torch, m, fn, args.steps, args.warmup)
+            counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
+            work = algorithmic_work(w, counts)
+            wbytes = work["active_experts"] * (work["per_expert_w1_bytes"] + work["per_expert_w2_bytes"])
+            gbs = wbytes / (ms / 1e3) / 1e9
+            row[path] = {"ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "weight_GB_per_s": gbs,
+                         "hbm_frac": gbs / HBM_PEAK_GBS}
+            log(f"# decode shapes T={T} {path}: {ms * 1e3:.1f} us, {work['active_experts']} experts, "
+                f"{gbs:.0f} GB/s of weights")
+        row.update(active_experts=work["active_experts"], weight_bytes=wbytes)
+        out[str(T)] = row
     return out
 
 

@@ -45,4 +45,13 @@ hipError_t launch_permute(const int32_t* ids, const float* w, int T, int k, int 
 // one-workgroup permutation (same results; hist and rank are not used).
 constexpr int kSmallRouteAssign = 4096;
 
+// Batches of at most kSmallFusedRouteTokens tokens (k <= 64) route and permute
+// in that one workgroup: top-k of router logits [T, E] into ids / w [T, k],
+// then the permutation as launch_permute does it.
+constexpr int kSmallFusedRouteTokens = 16;
+constexpr int kSmallFusedRouteAssign = kSmallFusedRouteTokens * 64;
+hipError_t launch_route_permute_small(const float* logits, int T, int E, int k, int32_t* ids, float* w, int off,
+                                      int L, int32_t* offsets, int32_t* sorted_assign, float* sorted_w, Tile* tiles,
+                                      int32_t* num_tiles, int bm, hipStream_t stream);
+
 }  // namespace moe_mx

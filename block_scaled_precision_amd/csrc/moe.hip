@@ -16,6 +16,7 @@
 
 #include "gemm.h"
 #include "internal.h"
+#include "micro.h"
 #include "mx_device.h"
 
 namespace moe_mx {
@@ -184,14 +185,26 @@ static int dense_tiled_rows(int M, int N, bool fc1, int grid) {
   return best;
 }
 
+// The small-batch path (micro.hip): bf16 activations and E2M1 weights, at
+// most kMicroMaxTokens tokens and kMicroMaxAssign assignments, H a multiple
+// of 1024 (two K halves of 512-K FC1 steps), I and I_shared multiples of 256,
+// and the batch's x rows within the LDS of a workgroup.
+static bool micro_ok(const moe_problem_t& p) {
+  return p.act == MOE_ACT_BF16 && p.w_fmt == MX_E2M1 && p.T >= 1 && p.T <= kMicroMaxTokens &&
+         (int64_t)p.T * p.k <= kMicroMaxAssign && p.H % kMicroHMultiple == 0 && p.I % 256 == 0 && p.I_shared % 256 == 0 &&
+         micro_fc1_lds(p.T, p.H) + kMicroFc1StaticLds <= 160 * 1024;
+}
+
 struct FusedPlan {
   int L, off;
   int64_t A;
+  bool micro;
   Fc routed, shared;
   int bm;         // M-tile height of the routed tile list
   int shared_bm;  // M-tile height of the shared expert on the mid-M kernel
   int nblk, max_tiles;
-  size_t ids, w, rank, hist, offsets, sorted, sorted_w, tiles, ntiles, xq, xs, h, hsc, hs, hssc, obuf, sbuf, total;
+  size_t ids, w, rank, hist, offsets, sorted, sorted_w, tiles, ntiles, xq, xs, h, hsc, hs, hssc, obuf, sbuf, micro_list,
+      total;
 };
 
 static FusedPlan plan(const moe_problem_t& p) {
@@ -268,6 +281,8 @@ static FusedPlan plan(const moe_problem_t& p) {
   f.hssc = (Is && mx) ? take(T * Is / 32) : 0;
   f.obuf = take(f.A * H * 2);
   f.sbuf = Is ? take(T * H * 2) : 0;
+  f.micro = (p.flags & MOE_FLAG_FUSED_SMALL_BATCH) != 0;
+  f.micro_list = take(sizeof(MicroList));
   f.total = o;
   return f;
 }
@@ -281,6 +296,7 @@ static moe_status_t validate(const moe_problem_t* p, const moe_tensors_t* t) {
   if (p->act != MOE_ACT_BF16 && p->act != MOE_ACT_MXFP8) return MOE_ERR_INVALID_ARG;
   if (p->act_fn != MOE_FN_SILU && p->act_fn != MOE_FN_RELU2 && p->act_fn != MOE_FN_SWIGLU_OAI)
     return MOE_ERR_INVALID_ARG;
+  if (p->flags & ~MOE_FLAG_FUSED_SMALL_BATCH) return MOE_ERR_INVALID_ARG;
   const int L = p->local_num_experts == 0 ? p->E : p->local_num_experts;
   if (p->local_expert_offset < 0 || L < 0 || (int64_t)p->local_expert_offset + L > p->E)
     return MOE_ERR_INVALID_ARG;
@@ -302,6 +318,7 @@ static moe_status_t validate(const moe_problem_t* p, const moe_tensors_t* t) {
   }
   // valid, but outside what the kernels implement
   if (p->w_fmt == MX_E4M3) return MOE_ERR_UNSUPPORTED;
+  if ((p->flags & MOE_FLAG_FUSED_SMALL_BATCH) && !micro_ok(*p)) return MOE_ERR_UNSUPPORTED;
   if (p->H % 128 || p->I % 128 || p->I_shared % 128) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -391,6 +408,11 @@ extern "C" moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int
   char* ws = (char*)workspace;
   int32_t* hist = (int32_t*)ws;
   int32_t* rank = (int32_t*)(ws + align_up(nblk * E * 4, 256));
+  if (T <= kSmallFusedRouteTokens && k <= 64)
+    return launch_route_permute_small(logits, T, E, k, topk_ids, topk_w, 0, E, expert_offsets, sorted_assign,
+                                      nullptr, nullptr, nullptr, 0, stream) == hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
   if (launch_topk(logits, T, E, k, topk_ids, topk_w, stream) != hipSuccess) return MOE_ERR_HIP;
   if (launch_permute(topk_ids, nullptr, T, k, 0, E, hist, rank, expert_offsets, sorted_assign, nullptr, nullptr,
                      nullptr, 0,
@@ -550,10 +572,69 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   };
   if (!mark(MOE_STAGE_ROUTE)) return MOE_ERR_HIP;
 
+  if (f.micro) {
+    // small batch: routing + FC1 in one kernel, FC2 + combine (+ shared) in another
+    const int64_t bh = (int64_t)H / 2, bi = (int64_t)I / 2;
+    MicroArgs m = {};
+    m.logits = t->topk_ids_in ? nullptr : t->router_logits;
+    m.ids_in = t->topk_ids_in;
+    m.w_in = t->topk_w_in;
+    m.T = T;
+    m.E = p->E;
+    m.k = k;
+    m.off = f.off;
+    m.L = f.L;
+    m.ids_out = t->topk_ids_out;
+    m.w_out = t->topk_w_out;
+    m.x = t->x;
+    m.H = H;
+    m.I = I;
+    m.Is = Is;
+    m.act_fn = p->act_fn;
+    m.w1 = t->w1;
+    m.s1 = t->w1_scale;
+    m.w1_estride = 2 * (int64_t)I * bh;
+    m.s1_estride = 2 * (int64_t)I * (H / 32);
+    m.ws1 = t->ws1;
+    m.ss1 = t->ws1_scale;
+    m.h = (uint16_t*)(ws + f.h);
+    m.hs = Is ? (uint16_t*)(ws + f.hs) : nullptr;
+    m.list = (MicroList*)(ws + f.micro_list);
+    m.w2 = t->w2;
+    m.s2 = t->w2_scale;
+    m.w2_estride = (int64_t)H * bi;
+    m.s2_estride = (int64_t)H * (I / 32);
+    m.ws2 = t->ws2;
+    m.ss2 = t->ws2_scale;
+    m.shared_weight = p->shared_weight;
+    m.y = (uint16_t*)t->y;
+    // stages: routing, permutation and FC1 are the first kernel; FC2, the
+    // shared expert and the combine the second
+    if (!mark(MOE_STAGE_PERMUTE) || !mark(MOE_STAGE_QUANT_X) || !mark(MOE_STAGE_FC1)) return MOE_ERR_HIP;
+    const hipEvent_t fc2 = t->stage_events ? t->stage_events[MOE_STAGE_FC2] : nullptr;
+    if (launch_micro(m, device_cus(), stream, fc2) != hipSuccess) return MOE_ERR_HIP;
+    if (!mark(MOE_STAGE_SHARED) || !mark(MOE_STAGE_FINALIZE) || !mark(MOE_NUM_STAGES)) return MOE_ERR_HIP;
+    return MOE_OK;
+  }
+
   // 1. routing
   const int32_t* ids;
   const float* wts;
-  if (t->topk_ids_in) {
+  int32_t* sorted = (int32_t*)(ws + f.sorted);
+  Tile* tiles = (Tile*)(ws + f.tiles);
+  int32_t* ntiles = (int32_t*)(ws + f.ntiles);
+  float* sorted_w = (float*)(ws + f.sorted_w);
+  // a few tokens: top-k and the permutation in one workgroup
+  const bool fused_route = !t->topk_ids_in && T <= kSmallFusedRouteTokens && k <= 64;
+  if (fused_route) {
+    int32_t* ids_w = t->topk_ids_out ? t->topk_ids_out : (int32_t*)(ws + f.ids);
+    float* w_w = t->topk_w_out ? t->topk_w_out : (float*)(ws + f.w);
+    if (!ok(launch_route_permute_small(t->router_logits, T, p->E, k, ids_w, w_w, f.off, f.L,
+                                       (int32_t*)(ws + f.offsets), sorted, sorted_w, tiles, ntiles, f.bm, stream)))
+      return MOE_ERR_HIP;
+    ids = ids_w;
+    wts = w_w;
+  } else if (t->topk_ids_in) {
     ids = t->topk_ids_in;
     wts = t->topk_w_in;
     if (t->topk_ids_out || t->topk_w_out) {
@@ -567,13 +648,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     ids = ids_w;
     wts = w_w;
   }
-  // 2. permutation by local expert + tile list
+  // 2. permutation by local expert + tile list (done above for a few tokens)
   if (!mark(MOE_STAGE_PERMUTE)) return MOE_ERR_HIP;
-  int32_t* sorted = (int32_t*)(ws + f.sorted);
-  Tile* tiles = (Tile*)(ws + f.tiles);
-  int32_t* ntiles = (int32_t*)(ws + f.ntiles);
-  float* sorted_w = (float*)(ws + f.sorted_w);
-  if (!ok(launch_permute(ids, wts, T, k, f.off, f.L, (int32_t*)(ws + f.hist), (int32_t*)(ws + f.rank),
+  if (!fused_route &&
+      !ok(launch_permute(ids, wts, T, k, f.off, f.L, (int32_t*)(ws + f.hist), (int32_t*)(ws + f.rank),
                          (int32_t*)(ws + f.offsets), sorted, sorted_w, tiles, ntiles, f.bm, stream)))
     return MOE_ERR_HIP;
   // 3. MXFP8 activations

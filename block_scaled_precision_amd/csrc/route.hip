@@ -169,21 +169,45 @@ __global__ __launch_bounds__(256) void k_scatter(const int32_t* __restrict__ ids
 // Small batches (T <= 64 tokens, T*k <= kSmallRouteAssign): the three steps
 // of the permutation in one workgroup of 16 waves, with the same results: the
 // tokens are one token block, so an expert's mask of tokens gives its count
-// and, below a token, that token's rank.
-__global__ __launch_bounds__(1024) void k_permute_small(const int32_t* __restrict__ ids, const float* __restrict__ w,
+// and, below a token, that token's rank.  With NS > 0 (at most 16 tokens,
+// k <= 64) the workgroup also routes: wave t takes the top-k of token t
+// straight into LDS (one launch instead of two), writing the ids and weights
+// out as k_topk would.
+template <int NS>
+__global__ __launch_bounds__(1024) void k_permute_small(const float* __restrict__ logits, int E,
+                                                        int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+                                                        const int32_t* __restrict__ ids, const float* __restrict__ w,
                                                         int T, int k, int off, int L, int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ sorted_assign,
                                                         float* __restrict__ sorted_w, Tile* __restrict__ tiles,
                                                         int32_t* __restrict__ num_tiles, int bm) {
   __shared__ unsigned long long mask[kMaxExperts];
   __shared__ int32_t s_ids[kSmallRouteAssign];
+  __shared__ float s_w[NS > 0 ? kSmallFusedRouteAssign : 1];
   __shared__ int32_t s_a[kMaxExperts];
   __shared__ int32_t s_b[kMaxExperts];
   __shared__ int32_t s_start[kMaxExperts];
   const int e = threadIdx.x;  // one thread per local expert in the scan
   const int A = T * k;
   mask[e] = 0ull;
-  for (int a = e; a < A; a += 1024) s_ids[a] = ids[a];
+  if constexpr (NS > 0) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (wv < T) {
+      TopkToken<NS> tk(logits + (int64_t)wv * E, E, lane);
+      int my_e;
+      float my_v;
+      tk.select(E, 0, k, lane, my_e, my_v);
+      if (lane < k) {
+        const float wt = expf(my_v - tk.top) * (1.0f / tk.sum);
+        s_ids[wv * k + lane] = my_e;
+        s_w[wv * k + lane] = wt;
+        ids_out[wv * k + lane] = my_e;
+        w_out[wv * k + lane] = wt;
+      }
+    }
+  } else {
+    for (int a = e; a < A; a += 1024) s_ids[a] = ids[a];
+  }
   __syncthreads();
   for (int a = e; a < A; a += 1024) {
     const int el = s_ids[a] - off;
@@ -230,16 +254,34 @@ __global__ __launch_bounds__(1024) void k_permute_small(const int32_t* __restric
     const unsigned long long below = t ? (~0ull >> (64 - t)) : 0ull;
     const int32_t pos = s_start[el] + __popcll(mask[el] & below);
     sorted_assign[pos] = a;
-    if (sorted_w) sorted_w[pos] = w[a];
+    if (sorted_w) sorted_w[pos] = NS > 0 ? s_w[a] : w[a];
   }
+}
+
+hipError_t launch_route_permute_small(const float* logits, int T, int E, int k, int32_t* ids, float* w, int off,
+                                      int L, int32_t* offsets, int32_t* sorted_assign, float* sorted_w, Tile* tiles,
+                                      int32_t* num_tiles, int bm, hipStream_t stream) {
+  const int ns = (E + 63) / 64;
+  const int b = tiles ? bm : 0;
+#define MOE_ROUTE_SMALL(N)                                                                                      \
+  k_permute_small<N><<<1, 1024, 0, stream>>>(logits, E, ids, w, nullptr, nullptr, T, k, off, L, offsets,     \
+                                             sorted_assign, sorted_w, tiles, num_tiles, b)
+  if (ns <= 1) MOE_ROUTE_SMALL(1);
+  else if (ns <= 2) MOE_ROUTE_SMALL(2);
+  else if (ns <= 4) MOE_ROUTE_SMALL(4);
+  else if (ns <= 6) MOE_ROUTE_SMALL(6);
+  else if (ns <= 8) MOE_ROUTE_SMALL(8);
+  else MOE_ROUTE_SMALL(16);
+#undef MOE_ROUTE_SMALL
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t* ids, const float* w, int T, int k, int off, int L, int32_t* hist,
                           int32_t* rank, int32_t* offsets, int32_t* sorted_assign, float* sorted_w, Tile* tiles,
                           int32_t* num_tiles, int bm, hipStream_t stream) {
   if (T <= 64 && (int64_t)T * k <= kSmallRouteAssign) {
-    k_permute_small<<<1, 1024, 0, stream>>>(ids, w, T, k, off, L, offsets, sorted_assign, sorted_w, tiles,
-                                            num_tiles, tiles ? bm : 0);
+    k_permute_small<0><<<1, 1024, 0, stream>>>(nullptr, 0, nullptr, nullptr, ids, w, T, k, off, L, offsets,
+                                               sorted_assign, sorted_w, tiles, num_tiles, tiles ? bm : 0);
     return hipGetLastError();
   }
   const int nblk = (T + 63) / 64;

@@ -40,7 +40,7 @@ class MoeProblem(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("w_fmt", ctypes.c_int),
                 ("act", ctypes.c_int), ("I_shared", ctypes.c_int32), ("shared_weight", ctypes.c_float),
                 ("local_expert_offset", ctypes.c_int32), ("local_num_experts", ctypes.c_int32),
-                ("act_fn", ctypes.c_int)]
+                ("act_fn", ctypes.c_int), ("flags", ctypes.c_uint32)]
 
 
 MOE_NUM_STAGES = 7
@@ -269,10 +269,14 @@ class MoeWeights:
     ws2_scale: torch.Tensor | None = None
 
 
+FLAG_FUSED_SMALL_BATCH = 1  # MOE_FLAG_FUSED_SMALL_BATCH
+
+
 def make_problem(T, H, I, E, k, fmt, act, I_shared=0, shared_weight=1.0, local_offset=0, local_count=0,
-                 act_fn="silu"):
+                 act_fn="silu", fused_small_batch=False):
     return MoeProblem(T, H, I, E, k, MX_FORMATS[fmt], ACTS[act], I_shared, shared_weight,
-                      local_offset, local_count, ACT_FNS[act_fn])
+                      local_offset, local_count, ACT_FNS[act_fn],
+                      FLAG_FUSED_SMALL_BATCH if fused_small_batch else 0)
 
 
 def moe_fused_workspace_bytes(problem: MoeProblem) -> int:

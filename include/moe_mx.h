@@ -181,7 +181,22 @@ typedef struct {
   int32_t local_expert_offset; /* first expert held by this call (TokenSpeed SiTU    */
   int32_t local_num_experts;   /* page, "Supported contract"); 0 means all E         */
   moe_act_fn_t act_fn;         /* gated activation of every expert (0 = SiLU)       */
+  uint32_t flags;              /* MOE_FLAG_* (0: defaults)                           */
 } moe_problem_t;
+
+/* Flags of moe_problem_t.
+ * MOE_FLAG_FUSED_SMALL_BATCH: run the two-launch small-batch path
+ *   (mxfp6-sm120 page, "Execution model": allocation-free routing, split W1,
+ *   fused W2 routed/shared reduction): every FC1 workgroup routes the batch
+ *   itself and FC2 adds the routed and shared outputs per token in fp32, so
+ *   y is ONE bf16 rounding of the whole sum (the default path rounds each
+ *   weighted expert row first).  Requires bf16 activations, E2M1 weights,
+ *   T <= 8, T*k <= 64, H % 512 == 0, I and I_shared multiples of 256 and
+ *   T*(2H+16) + 24 KiB of LDS <= 160 KiB; otherwise MOE_ERR_UNSUPPORTED.
+ *   Its kernels load the weights straight into registers; on MI355X they
+ *   stream them more slowly than the default path's LDS rings, so this is an
+ *   option, not the default. */
+#define MOE_FLAG_FUSED_SMALL_BATCH 1u
 
 /* Tensors of one call.  W1/W2 hold only the local experts: expert index
  * local_expert_offset + i is stored at position i. */

@@ -87,6 +87,21 @@ def test_invalid_tensors_rejected_on_host(tkw, status):
     assert L.moe_fused(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(1 << 20), 1 << 40, None) == status
 
 
+def test_flags_and_activation_validation():
+    m, L = _lib()
+    t = _tensors(m)
+    for fields, status in [(dict(flags=2), 1), (dict(act_fn=3), 1),
+                           (dict(flags=1, T=9), 2), (dict(flags=1, act="mxfp8"), 2), (dict(flags=1), 2)]:
+        p = _problem(m, T=fields.pop("T", 16), act=fields.pop("act", "bf16"))
+        for k_, v in fields.items():
+            setattr(p, k_, v)
+        # (flags=1 with H = 256: not a multiple of 512 -> unsupported)
+        assert L.moe_fused(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(1 << 20), 1 << 40, None) == status
+    p = _problem(m, T=4, H=1024)
+    p.flags = 1
+    assert L.moe_fused(ctypes.byref(p), ctypes.byref(t), ctypes.c_void_p(1 << 20), 1 << 40, None) == 4
+
+
 def test_workspace_checks():
     m, L = _lib()
     p = _problem(m)

@@ -28,7 +28,10 @@ from tests.helpers import assert_y_close, gpu_weights, oracle_rows, print_flush
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
 
-NAMES = ["decode_w4a16", "prefill_w4a8", "skew_w4a16", "w6a8_shared"]
+NAMES = ["decode_w4a16", "decode_t1", "decode_t2", "decode_t4", "decode_t8", "prefill_w4a8", "skew_w4a16",
+         "w6a8_shared"]
+# the decode shapes at batches of 1 to 8 tokens (the small-batch path)
+SMALL = {f"decode_t{T}": gen.scaled(gen.WORKLOADS["decode_w4a16"], name=f"decode_t{T}", T=T) for T in (1, 2, 4, 8)}
 _oracle_cache = {}
 _gpu = {}
 
@@ -64,7 +67,7 @@ def _tile_tokens(ids, E, k, bm):
 
 def _sample(name, w, o_ids):
     T = w.T
-    if name == "decode_w4a16":
+    if name == "decode_w4a16" or name in SMALL:
         return list(range(T))
     if name == "prefill_w4a8":
         toks, ntiles = _tile_tokens(o_ids, w.E, w.k, 192)
@@ -86,7 +89,7 @@ def _sample(name, w, o_ids):
 def test_full_size_layer(name):
     from block_scaled_precision_amd import moe_mx as m
 
-    w = gen.WORKLOADS[name]
+    w = SMALL[name] if name in SMALL else gen.WORKLOADS[name]
     print_flush(f"full-size {name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} {w.wfmt}/{w.act} Is={w.I_shared}")
     gw = _gpu_weights(w)
     logits = gen.router_logits(w, device="cuda")
@@ -121,6 +124,15 @@ def test_full_size_layer(name):
     got = y[toks].float().cpu().numpy()
     mr, rr = assert_y_close(got, ref, f"{name} tokens {toks[:8]}...")
     print_flush(f"  {len(toks)} tokens, {n_exp} experts: max_rel={mr:.3e} rms_rel={rr:.3e}")
+    if name in SMALL:
+        # the fused small-batch path on the same batch
+        pf = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, fused_small_batch=True)
+        fids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+        yf = m.moe_fused(pf, x, gw, router_logits=logits, topk_ids_out=fids)
+        torch.cuda.synchronize()
+        assert np.array_equal(fids.cpu().numpy(), o_ids)
+        mr, rr = assert_y_close(yf.float().cpu().numpy(), ref, f"{name} fused small batch")
+        print_flush(f"  fused small-batch path: max_rel={mr:.3e} rms_rel={rr:.3e}")
     del y
     if name == NAMES[-1]:
         _gpu.clear()
