@@ -118,4 +118,26 @@ __device__ __forceinline__ float gated_act(int fn, float g, float u) {
   return silu_mul(g, u);
 }
 
+// SiLU(g) * u with the hardware exp2 and reciprocal (about 2 ulp in fp32;
+// the result is then rounded to E4M3, 3 mantissa bits).
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504f)) * u;
+}
+// the gated activation, fixed per instantiation (a run-time choice in this
+// epilogue made the compiler spill registers in the step loop): SiLU as
+// above, the other forms as in every other kernel
+template <int ACT>
+__device__ __forceinline__ float act_mul(float g, float u) {
+  return ACT == MOE_FN_SILU ? silu_mul_fast(g, u) : gated_act(ACT, g, u);
+}
+
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xb1, 0xf, 0xf, true));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4e, 0xf, 0xf, true));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xf, 0xf, true));  // row_ror 4
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xf, 0xf, true));  // row_ror 8
+  return v;
+}
+
 }  // namespace moe_mx
