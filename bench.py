@@ -71,7 +71,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="all", help="one workload name, or 'all' (default)")
+    ap.add_argument("--workload", default="all",
+                    help="one workload name, 'all' (default), or 'small_batches' / 'dense_gemm' "
+                         "for those parts of the default run alone")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-tokens", type=int, default=16,
                     help="tokens of the decode workload the CPU oracle runs on")
@@ -418,6 +420,14 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.workload == "small_batches":
+        w = gen.WORKLOADS[HEADLINE]
+        mw = build_weights(torch, m, gen, w, args.seed)
+        print(json.dumps({"small_batches": small_batches(torch, np, m, gen, mw, args)}), flush=True)
+        return
+    if args.workload == "dense_gemm":
+        print(json.dumps({"dense_gemm": dense_gemms(torch, m, gen, args)}), flush=True)
         return
     names = ORDER if args.workload == "all" else (args.workload,)
     head = HEADLINE if HEADLINE in names else names[0]
