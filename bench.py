@@ -280,12 +280,27 @@ def event_median(torch, m, fn, steps, warmup):
     return statistics.median([ev.elapsed_ms(i, i + 1) for i in range(steps)])
 
 
+def graph_median(torch, m, fn, steps, warmup):
+    """Median HIP-event time (ms) of replays of fn() captured in a HIP graph
+    (torch.cuda.graph), and the graph (so that its output can be checked)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up outside the capture
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return event_median(torch, m, g.replay, steps, warmup), g
+
+
 def small_batches(torch, np, m, gen, mw, args, batches=(1, 2, 4, 8)):
     """The decode shapes (H=7168, I=2048, E=384 resident experts, top-8, bf16
     activations) at batches of 1 to 8 tokens, on the default path and on the
-    fused small-batch path: the whole layer per call, and the packed weights
-    of the experts the batch routes to (what the call must stream from HBM)
-    per second against the HBM peak."""
+    fused small-batch path: the whole layer per call, eager and as a HIP graph
+    replay (no launch gaps from the host), and the packed weights of the
+    experts the batch routes to (what the call must stream from HBM) per
+    second against the HBM peak."""
     base = gen.WORKLOADS[HEADLINE]
     out = {}
     for T in batches:
@@ -301,14 +316,22 @@ def small_batches(torch, np, m, gen, mw, args, batches=(1, 2, 4, 8)):
             fn = lambda: m.moe_fused(prob, x, mw, router_logits=logits, y=y, workspace=ws,  # noqa: E731
                                      topk_ids_out=ids)
             ms = event_median(torch, m, fn, args.steps, args.warmup)
+            y_eager = y.clone()
+            ms_graph, g = graph_median(torch, m, fn, args.steps, args.warmup)
+            torch.cuda.synchronize()
+            if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+                raise RuntimeError(f"graph replay differs from the eager call (T={T}, {path})")
+            del g
             counts = torch.bincount(ids.flatten().long(), minlength=w.E).cpu().numpy()
             work = algorithmic_work(w, counts)
             wbytes = work["active_experts"] * (work["per_expert_w1_bytes"] + work["per_expert_w2_bytes"])
             gbs = wbytes / (ms / 1e3) / 1e9
+            gbs_g = wbytes / (ms_graph / 1e3) / 1e9
             row[path] = {"ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "weight_GB_per_s": gbs,
-                         "hbm_frac": gbs / HBM_PEAK_GBS}
-            log(f"# decode shapes T={T} {path}: {ms * 1e3:.1f} us, {work['active_experts']} experts, "
-                f"{gbs:.0f} GB/s of weights")
+                         "hbm_frac": gbs / HBM_PEAK_GBS, "graph_ms_per_step": ms_graph,
+                         "graph_hbm_frac": gbs_g / HBM_PEAK_GBS}
+            log(f"# decode shapes T={T} {path}: {ms * 1e3:.1f} us ({ms_graph * 1e3:.1f} us as a graph replay), "
+                f"{work['active_experts']} experts, {gbs:.0f} GB/s of weights ({gbs_g:.0f} replayed)")
         row.update(active_experts=work["active_experts"], weight_bytes=wbytes)
         out[str(T)] = row
     return out

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
       tiles[tstart + i] = tl;
     }
   }
-  if (e == 0 && bm > 0) *num_tiles = s_b[1023];
+  if (e == 0 && bm > 0) *num_tiles = s_b[16 + 15];
 }
 
 // sorted_assign[pos] = a and, if requested, sorted_w[pos] = w[a] (the routing
@@ -215,26 +215,51 @@ __global__ __launch_bounds__(1024) void k_permute_small(const float* __restrict_
   }
   __syncthreads();
   // counts, inclusive scans of counts and tile counts over the experts,
-  // offsets and tiles (as k_scan with one token block)
+  // offsets and tiles (as k_scan with one token block): each wave scans its
+  // 64 experts across lanes, wave 0 scans the 16 wave totals
   const int32_t count = e < L ? __popcll(mask[e]) : 0;
   const int32_t ntile = (e < L && bm > 0) ? (count + bm - 1) / bm : 0;
-  s_a[e] = count;
-  s_b[e] = ntile;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int32_t a = e >= d ? s_a[e - d] : 0;
-    const int32_t b = e >= d ? s_b[e - d] : 0;
-    __syncthreads();
-    s_a[e] += a;
-    s_b[e] += b;
-    __syncthreads();
+  const int lane_e = e & 63, wv_e = e >> 6;
+  int32_t inc_a = count, inc_b = ntile;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t a = __shfl_up(inc_a, d), b = __shfl_up(inc_b, d);
+    if (lane_e >= d) {
+      inc_a += a;
+      inc_b += b;
+    }
   }
-  const int32_t start = s_a[e] - count;
+  if (lane_e == 63) {
+    s_a[wv_e] = inc_a;
+    s_b[wv_e] = inc_b;
+  }
+  __syncthreads();
+  if (wv_e == 0) {
+    int32_t ta = lane_e < 16 ? s_a[lane_e] : 0, tb = lane_e < 16 ? s_b[lane_e] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int32_t a = __shfl_up(ta, d), b = __shfl_up(tb, d);
+      if (lane_e >= d) {
+        ta += a;
+        tb += b;
+      }
+    }
+    if (lane_e < 16) {
+      s_a[16 + lane_e] = ta;  // inclusive totals through wave lane_e
+      s_b[16 + lane_e] = tb;
+    }
+  }
+  __syncthreads();
+  if (wv_e > 0) {
+    inc_a += s_a[16 + wv_e - 1];
+    inc_b += s_b[16 + wv_e - 1];
+  }
+  const int32_t start = inc_a - count;
   s_start[e] = start;
   if (e < L) {
     offsets[e] = start;
-    if (e == L - 1) offsets[L] = s_a[e];
-    const int32_t tstart = s_b[e] - ntile;
+    if (e == L - 1) offsets[L] = inc_a;
+    const int32_t tstart = inc_b - ntile;
     for (int i = 0; i < ntile; ++i) {
       const int32_t r0 = i * bm;
       Tile tl;
@@ -245,7 +270,7 @@ __global__ __launch_bounds__(1024) void k_permute_small(const float* __restrict_
       tiles[tstart + i] = tl;
     }
   }
-  if (e == 0 && bm > 0) *num_tiles = s_b[1023];
+  if (e == 0 && bm > 0) *num_tiles = s_b[16 + 15];
   __syncthreads();
   for (int a = e; a < A; a += 1024) {
     const int el = s_ids[a] - off;

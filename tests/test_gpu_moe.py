@@ -16,6 +16,8 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a
 CASES = {
     "tiny_w4a16": gen.WORKLOADS["tiny_w4a16"],
     "decode_w4a16_small": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=64, H=512, I=256, E=48),
+    # a few tokens: top-k and permutation in one launch (and the fused small-batch path on request)
+    "decode_w4a16_t4": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=4, H=512, I=256, E=48),
     "prefill_w4a8_small": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=300, H=512, I=512, E=16, k=4),
     "skew_w4a16_small": gen.scaled(gen.WORKLOADS["skew_w4a16"], T=256, H=256, I=256, E=32, k=4),
     "w6a8_shared_small": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=100, H=512, I=512, E=24, k=6,
@@ -322,13 +324,15 @@ def test_tensor_parallel_shards_sum_to_full_layer(name, n):
     assert_y_close(sum(parts), full, f"{name} TP shard sum")
 
 
-@pytest.mark.parametrize("name", ["decode_w4a16_small", "w6a8_shared_small", "w4a8_wide_multi_tile"])
-def test_graph_capture_and_replay(name):
+@pytest.mark.parametrize("name,fused", [("decode_w4a16_small", False), ("decode_w4a16_t4", False),
+                                        ("decode_w4a16_t4", True), ("w6a8_shared_small", False),
+                                        ("w4a8_wide_multi_tile", False)])
+def test_graph_capture_and_replay(name, fused):
     """moe_fused captured in a HIP graph (torch.cuda.graph) and replayed: every
     replay, with new inputs copied in and eager work between replays, matches
     the eager call on the same inputs bit for bit, and the oracle."""
     w, gw, arrs, shared, x, logits, m = _prepare(name)
-    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared)
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared, fused_small_batch=fused)
     xs = [x.cuda(), (x.float() * -0.5).to(torch.bfloat16).cuda()]
     ls = [logits.cuda(), logits.flip(0).contiguous().cuda()]
     xb, lb = xs[0].clone(), ls[0].clone()
