@@ -355,7 +355,7 @@ def dense_gemms(torch, m, gen, args):
         a = gen.normal((M, K), args.seed, 30, device="cuda").to(torch.bfloat16)
         wq, sq = m.mx_quantize(gen.normal((N, K), args.seed, 31, device="cuda", std=0.02), fmt)
         c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
-        ws = torch.empty((max(m.mx_gemm_workspace_bytes(M, K, act), 1),), dtype=torch.uint8, device="cuda")
+        ws = torch.empty((max(m.mx_gemm_workspace_bytes(M, N, K, act, fmt), 1),), dtype=torch.uint8, device="cuda")
         fn = lambda: m.mx_gemm(a, wq, sq, fmt, act, c=c, workspace=ws)  # noqa: E731
         ms = event_median(torch, m, fn, args.steps, args.warmup)
         flops = 2.0 * M * N * K

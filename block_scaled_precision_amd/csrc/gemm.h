@@ -41,6 +41,11 @@ struct FcArgs {
   uint16_t* obuf;      // FC2: bf16 rows [A, N] (routed: row = assignment a, holding
                        // w(a) * o; dense: row = token, holding dense_weight * o),
                        // the product taken in fp32 and rounded once (RNE)
+  // dense FC2 on the small-M kernel only: K split into ksplit equal ranges
+  // (ksplit > 1), each item writing its unscaled fp32 sum to part
+  // [ksplit, dense_rows, N] instead of obuf; 0 or 1 = no split
+  int ksplit;
+  float* part;
 };
 
 // Columns of N covered by one wave of the stream kernels.
@@ -81,6 +86,10 @@ hipError_t launch_fc_wide(const FcArgs& p, bool fc1, int grid, hipStream_t st);
 // Requires K % kSmallK == 0.
 constexpr int kSmallK = 256;
 hipError_t launch_fc_small(const FcArgs& p, bool fc1, int grid, hipStream_t st);
+// y = bf16_RNE(alpha * sum over s of part[s]) for the ksplit partial sums of a
+// split dense GEMM, summed in ascending s; n4 = rows * N / 4 (N % 4 == 0)
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int64_t n4, float alpha, uint16_t* y,
+                                hipStream_t st);
 
 // Mid-M variant for bf16 activations and E2M1 weights when experts see many
 // rows: M-tiles of up to `rows` rows (kMidRows or kMidRowsHigh), N-blocks of

@@ -87,17 +87,19 @@ __device__ __forceinline__ int wb_off(int r, int c) { return r * BROW + 16 * (c 
 __device__ __forceinline__ int wa_off(int r, int c) { return r * (2 * SBK) + 16 * (c ^ (r & 7)); }
 
 struct SGeom {
-  int expert, p0, rows, nb;
+  int expert, p0, rows, nb, ks;
 };
+// NB N-blocks and S K-ranges per M-tile (S > 1 only for split dense GEMMs)
 struct SSched {
-  int q, Q, NB, nk, my_items, total;
+  int q, Q, NB, S, nk, my_items, total;
 };
 
 __device__ __forceinline__ SGeom s_geom(const FcArgs& p, const SSched& sc, int li) {
   const int j = sc.q + li * sc.Q;
-  const int ti = j / sc.NB;
+  const int ti = j / (sc.NB * sc.S), r = j % (sc.NB * sc.S);
   SGeom g;
-  g.nb = j % sc.NB;
+  g.nb = r / sc.S;
+  g.ks = r % sc.S;
   if (p.dense_rows > 0) {
     g.expert = 0;
     g.p0 = SBM * ti;
@@ -206,7 +208,17 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
     } else {
       int orow[4];
       float wt[4];
-      if (p.dense_rows > 0) {
+      if (sc.S > 1) {
+        // split dense GEMM: this K range's unscaled fp32 sums
+        float* o = p.part + ((int64_t)it.ks * p.dense_rows + it.p0) * p.N + it.nb * SBN + 32 * w + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (4 * g + i < it.rows) {
+            o[(int64_t)(4 * g + i) * p.N] = acc[0][i];
+            o[(int64_t)(4 * g + i) * p.N + 16] = acc[1][i];
+          }
+        }
+      } else if (p.dense_rows > 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           orow[i] = it.p0 + 4 * g + i;
@@ -231,7 +243,7 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (4 * g + i < it.rows) {
+        if (sc.S == 1 && 4 * g + i < it.rows) {
           uint16_t* o = p.obuf + (int64_t)orow[i] * p.N + it.nb * SBN + 32 * w + r16;
           o[0] = f32_to_bf16_rne(wt[i] * acc[0][i]);
           o[16] = f32_to_bf16_rne(wt[i] * acc[1][i]);
@@ -260,8 +272,9 @@ __device__ __forceinline__ void small_weights(const FcArgs& p, const SSched& sc,
   const uint8_t* ssrc[SG::COPIES];
   auto setup = [&](int li) {
     const SGeom it = s_geom(p, sc, li);
-    const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride;
-    const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride;
+    const int64_t k0 = (int64_t)it.ks * sc.nk * SBK;  // first k of the item's range
+    const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride + k0 / 2;
+    const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride + k0 / 32;
 #pragma unroll
     for (int i = 0; i < kBData; ++i) {
       const int t = kBData * bw + i;  // 1-KB copy index within the stage
@@ -343,7 +356,7 @@ __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched&
         row = tr;
       }
       const int c = (lane % CPA) ^ (lr & 7);  // chunk for this lane's LDS slot
-      src[i] = (const uint8_t*)p.a + row * (2 * (int64_t)K) + 16 * c;
+      src[i] = (const uint8_t*)p.a + row * (2 * (int64_t)K) + 2 * (int64_t)it.ks * sc.nk * SBK + 16 * c;
     }
   };
   int li = 0, ls = 0, issued = 0;
@@ -372,12 +385,13 @@ template <bool FC1, int GS>
 __global__ __launch_bounds__(kThreadsS, 1) void k_fc_small(FcArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[L_SG + L_SG_SIZE];
   SSched sc;
-  sc.nk = p.K / SBK;
+  sc.S = p.ksplit > 1 ? p.ksplit : 1;
+  sc.nk = p.K / SBK / sc.S;
   sc.NB = p.nchunks;
   const int ntiles = p.dense_rows > 0 ? (p.dense_rows + SBM - 1) / SBM : *p.num_tiles;
   sc.q = blockIdx.x;
   sc.Q = gridDim.x;
-  const int nitems = ntiles * sc.NB;
+  const int nitems = ntiles * sc.NB * sc.S;
   sc.my_items = nitems > sc.q ? (nitems - sc.q + sc.Q - 1) / sc.Q : 0;
   sc.total = sc.my_items * sc.nk;
   if (sc.total == 0) return;
@@ -390,10 +404,37 @@ __global__ __launch_bounds__(kThreadsS, 1) void k_fc_small(FcArgs p) {
 template <bool FC1>
 static hipError_t launch_small_t(const FcArgs& p, int grid, hipStream_t st) {
   // scale groups: the largest of 4, 2, 1 stages that divides the stages of an item
-  const int nk = p.K / SBK;
+  const int nk = p.K / SBK / (p.ksplit > 1 ? p.ksplit : 1);
   if (nk % 4 == 0) k_fc_small<FC1, 4><<<grid, kThreadsS, 0, st>>>(p);
   else if (nk % 2 == 0) k_fc_small<FC1, 2><<<grid, kThreadsS, 0, st>>>(p);
   else k_fc_small<FC1, 1><<<grid, kThreadsS, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+// Sum of the K-range partials of a split dense GEMM: 4 columns per thread,
+// the ranges added in ascending order, then alpha, then one bf16 rounding.
+__global__ void k_splitk_reduce(const float4* __restrict__ part, int ksplit, int64_t n4, float alpha,
+                                uint2* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  float4 s = part[i];
+  for (int k = 1; k < ksplit; ++k) {
+    const float4 v = part[(int64_t)k * n4 + i];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  uint2 o;
+  o.x = (uint32_t)f32_to_bf16_rne(alpha * s.x) | ((uint32_t)f32_to_bf16_rne(alpha * s.y) << 16);
+  o.y = (uint32_t)f32_to_bf16_rne(alpha * s.z) | ((uint32_t)f32_to_bf16_rne(alpha * s.w) << 16);
+  y[i] = o;
+}
+
+hipError_t launch_splitk_reduce(const float* part, int ksplit, int64_t n4, float alpha, uint16_t* y,
+                                hipStream_t st) {
+  if (n4 <= 0) return hipSuccess;
+  k_splitk_reduce<<<(unsigned)((n4 + 255) / 256), 256, 0, st>>>((const float4*)part, ksplit, n4, alpha, (uint2*)y);
   return hipGetLastError();
 }
 

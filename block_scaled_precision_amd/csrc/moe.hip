@@ -460,10 +460,41 @@ static Fc dense_kind(int64_t M, int64_t N, int64_t K, bool mx, mx_elem_t wf, int
   return Fc::kStream;
 }
 
-extern "C" size_t mx_gemm_workspace_bytes(int64_t M, int64_t K, moe_act_t act) {
-  if (M < 0 || K <= 0 || K % 32) return 0;
-  if (act != MOE_ACT_MXFP8) return 0;
+// K split of a dense GEMM on the small-M kernel (bf16 activations, E2M1
+// weights, few rows): the number of equal K ranges, each of whole stages and at
+// least two, that best fills kSplitTargetItems workgroup items (ties: fewer
+// ranges); 1 when the items already fill them.  A function of the shape only,
+// so that the workspace size does not depend on the device.
+constexpr int kSplitTargetItems = 256;
+static int dense_ksplit(int64_t M, int64_t N, int64_t K, moe_act_t act, mx_elem_t wf) {
+  if (act != MOE_ACT_BF16 || wf != MX_E2M1 || M <= 0 || M >= kMidMinRowsPerExpert) return 1;
+  if (K % kSmallK || N % kSmallColsFc2 || N % 4) return 1;
+  const int64_t items = (M + kStreamRows - 1) / kStreamRows * (N / kSmallColsFc2);
+  if (items * 2 > kSplitTargetItems) return 1;
+  const int64_t nk = K / kSmallK;
+  int best = 1;
+  double best_fill = (double)items / kSplitTargetItems;
+  for (int64_t s = 2; s <= nk / 2 && s <= 64; ++s) {
+    if (nk % s) continue;
+    const int64_t n = items * s;
+    const double fill = (double)n / (double)(((n + kSplitTargetItems - 1) / kSplitTargetItems) * kSplitTargetItems);
+    if (fill > best_fill + 1e-9) {
+      best = (int)s;
+      best_fill = fill;
+    }
+  }
+  return best;
+}
+
+static size_t gemm_quant_bytes(int64_t M, int64_t K) {
   return align_up((size_t)(M * K), 256) + align_up((size_t)(M * K / 32), 256);
+}
+
+extern "C" size_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, moe_act_t act, mx_elem_t w_fmt) {
+  if (M < 0 || N <= 0 || K <= 0 || K % 32) return 0;
+  if (act == MOE_ACT_MXFP8) return gemm_quant_bytes(M, K);
+  const int s = dense_ksplit(M, N, K, act, w_fmt);
+  return s > 1 ? align_up((size_t)s * (size_t)M * (size_t)N * 4, 256) : 0;
 }
 
 extern "C" moe_status_t mx_gemm(const void* a, const uint8_t* a_scale, int64_t M, int64_t N, int64_t K,
@@ -483,9 +514,14 @@ extern "C" moe_status_t mx_gemm(const void* a, const uint8_t* a_scale, int64_t M
   if (w_fmt == MX_E4M3 || N % 8 || K % 128) return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
   const bool quant = act == MOE_ACT_MXFP8 && !a_scale;
-  const size_t need = quant ? mx_gemm_workspace_bytes(M, K, act) : 0;
+  const size_t need = quant ? gemm_quant_bytes(M, K) : 0;
   if (quant && (workspace_bytes < need || !workspace)) return MOE_ERR_WORKSPACE;
   if (quant && ((uintptr_t)workspace & 255u) != 0) return MOE_ERR_INVALID_ARG;
+  // a K split only when the caller's workspace holds its partial sums
+  int ksplit = dense_ksplit(M, N, K, act, w_fmt);
+  if (ksplit > 1 && (!workspace || ((uintptr_t)workspace & 255u) != 0 ||
+                     workspace_bytes < (size_t)ksplit * (size_t)M * (size_t)N * 4))
+    ksplit = 1;
   moe_status_t st = check_arch();
   if (st != MOE_OK) return st;
 
@@ -516,10 +552,17 @@ extern "C" moe_status_t mx_gemm(const void* a, const uint8_t* a_scale, int64_t M
   const int cols = fc_cols(kind, false, rows);
   g.nchunks = (int)((N + cols - 1) / cols);  // the stream kernels mask the last chunk's columns
   g.obuf = (uint16_t*)c;
+  if (kind == Fc::kSmall && ksplit > 1) {
+    g.ksplit = ksplit;
+    g.part = (float*)workspace;
+  }
   const int wf = w_fmt == MX_E2M1 ? 1 : 2;
   hipError_t e = hipSuccess;
   switch (kind) {
-    case Fc::kSmall: e = launch_fc_small(g, false, cus, stream); break;
+    case Fc::kSmall:
+      e = launch_fc_small(g, false, cus, stream);
+      if (e == hipSuccess && g.ksplit > 1) e = launch_splitk_reduce(g.part, g.ksplit, M * N / 4, alpha, (uint16_t*)c, stream);
+      break;
     case Fc::kMid: e = launch_fc_mid(g, false, rows, cus, stream); break;
     case Fc::kWide: e = launch_fc_wide(g, false, cus, stream); break;
     case Fc::kTiled: e = launch_fc_tiled(g, false, wf, rows, cus, stream); break;

@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.moe_fused_workspace_bytes.restype = sz
         L.moe_fused.argtypes = [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeTensors), vp, sz, vp]
         L.moe_fused.restype = ctypes.c_int
-        L.mx_gemm_workspace_bytes.argtypes = [i64, i64, ctypes.c_int]
+        L.mx_gemm_workspace_bytes.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int]
         L.mx_gemm_workspace_bytes.restype = sz
         L.mx_gemm.argtypes = [vp, vp, i64, i64, i64, ctypes.c_int, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp,
                               sz, vp]
@@ -210,8 +210,8 @@ def moe_route(logits: torch.Tensor, k: int, workspace: torch.Tensor | None = Non
 
 # ---------------------------------------------------------------- gemm ---
 
-def mx_gemm_workspace_bytes(M: int, K: int, act: str) -> int:
-    return lib().mx_gemm_workspace_bytes(M, K, ACTS[act])
+def mx_gemm_workspace_bytes(M: int, N: int, K: int, act: str, w_fmt: str) -> int:
+    return lib().mx_gemm_workspace_bytes(M, N, K, ACTS[act], MX_FORMATS[w_fmt])
 
 
 def mx_gemm(a: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor, fmt: str, act: str = "mxfp8",
@@ -241,7 +241,8 @@ def mx_gemm(a: torch.Tensor, w: torch.Tensor, w_scale: torch.Tensor, fmt: str, a
     if c is None:
         c = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     _require(c, "c", torch.bfloat16, (M, N))
-    need = mx_gemm_workspace_bytes(M, K, act) if a_scale is None else 0
+    # MXFP8 from bf16: the quantized A; bf16 with few rows: the K split's partial sums
+    need = mx_gemm_workspace_bytes(M, N, K, act, fmt) if a_scale is None else 0
     if workspace is None and need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
     if workspace is not None:

@@ -156,13 +156,19 @@ moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t k, int
  * w, w_scale  [N, K*b/8] packed codes and [N, K/32] E8M0 scales of w_fmt
  *          (MX_E2M1 or MX_E3M2), the canonical layout above.
  * c        [M, N] bf16 out, rows contiguous.
- * workspace   at least mx_gemm_workspace_bytes(M, K, act) bytes (0 unless A
- *          is quantized here), 256-byte aligned; contents need not be set.
+ * workspace   mx_gemm_workspace_bytes(M, N, K, act, w_fmt) bytes, 256-byte
+ *          aligned; contents need not be set.  It holds the quantized A
+ *          (MXFP8 from bf16; required), or, for few rows of bf16 A against
+ *          E2M1 weights (M < 32), the fp32 partial sums of a K split over
+ *          more workgroups (optional: with less workspace the GEMM runs
+ *          unsplit, with the same result up to the fp32 summation order).
+ *          The split's partial sums are added in a fixed order, so the
+ *          result stays deterministic.
  * Requires M >= 0 (0: no-op), K % 32 == 0, 16-byte aligned a, c, w (and
  * a_scale if given); N % 8 != 0, K % 128 != 0 or E4M3 weights give
  * MOE_ERR_UNSUPPORTED.  Deterministic.
  */
-size_t mx_gemm_workspace_bytes(int64_t M, int64_t K, moe_act_t act);
+size_t mx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, moe_act_t act, mx_elem_t w_fmt);
 moe_status_t mx_gemm(const void* a, const uint8_t* a_scale, int64_t M, int64_t N, int64_t K, moe_act_t act,
                      const uint8_t* w, const uint8_t* w_scale, mx_elem_t w_fmt, float alpha, void* c,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);

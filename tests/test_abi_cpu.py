@@ -167,8 +167,17 @@ def test_gemm_validation():
     assert call(a, None, 4, 64, 96, 0, a, a, 1, f, a, None, 0, None) == 2         # K % 128
     assert call(a, None, 4, 64, 128, 0, a, a, 3, f, a, None, 0, None) == 2        # E4M3 weights
     assert call(a, None, 4, 64, 128, 1, a, a, 1, f, a, None, 0, None) == 3        # no workspace
-    need = L.mx_gemm_workspace_bytes(4, 128, 1)
-    assert need >= 4 * 128 + 4 * 4 and L.mx_gemm_workspace_bytes(4, 128, 0) == 0
+    need = L.mx_gemm_workspace_bytes(4, 64, 128, 1, 1)
+    assert need >= 4 * 128 + 4 * 4 and L.mx_gemm_workspace_bytes(4, 64, 128, 0, 1) == 0
+    # bf16 x E2M1 with few rows: room for a K split's fp32 partial sums (a whole
+    # number of 256-K stages per range, at least two); none when the rows or
+    # column blocks already fill the workgroups, or for E3M2 weights
+    split = L.mx_gemm_workspace_bytes(8, 4096, 7168, 0, 1)
+    assert split >= 7 * 8 * 4096 * 4 and split % 256 == 0
+    assert L.mx_gemm_workspace_bytes(8, 4096, 7168, 0, 2) == 0
+    assert L.mx_gemm_workspace_bytes(64, 4096, 7168, 0, 1) == 0
+    assert L.mx_gemm_workspace_bytes(8, 65536, 7168, 0, 1) == 0
+    assert L.mx_gemm_workspace_bytes(8, 4096, 256, 0, 1) == 0
     assert call(a, None, 4, 64, 128, 1, a, a, 1, f, a, vp(1 << 20), need - 1, None) == 3
     assert call(a, a, 4, 64, 128, 1, a, a, 1, f, a, None, 0, None) == 4          # pre-quantized: no workspace
     assert call(None, None, 0, 64, 128, 0, None, None, 1, f, None, None, 0, None) == 0  # M = 0

@@ -34,7 +34,10 @@ EXACT = [
     (40, 136, 256, "e3m2", "mxfp8"),     # stream, K not a multiple of 512
     (100, 512, 512, "e2m1", "bf16"),     # mid-M (64-row tiles)
     (130, 256, 1024, "e2m1", "bf16"),    # mid-M (128-row tiles)
-    (8, 256, 1024, "e2m1", "bf16"),      # small-M
+    (8, 256, 1024, "e2m1", "bf16"),      # small-M, K split in 2 (partials summed after)
+    (5, 256, 2048, "e2m1", "bf16"),      # small-M, K split in 4
+    (17, 256, 1536, "e2m1", "bf16"),     # small-M, two M-tiles, K split in 3
+    (16, 512, 7168, "e2m1", "bf16"),     # small-M, K split in 14 (the decode K)
     (5, 72, 128, "e3m2", "bf16"),        # stream, E3M2 x bf16
     (1, 8, 128, "e2m1", "bf16"),         # one row, one 8-column block
 ]
@@ -83,6 +86,7 @@ RANDOM = [
     (96, 512, 1024, "e2m1", "bf16"),
     (7, 1000, 256, "e2m1", "mxfp8"),
     (3, 64, 384, "e3m2", "bf16"),
+    (8, 1024, 3584, "e2m1", "bf16"),     # small-M with a K split
 ]
 
 
@@ -111,3 +115,39 @@ def test_zero_rows_and_repeat():
     c2 = m.mx_gemm(a.cuda(), w.cuda(), s.cuda(), "e2m1", "mxfp8")
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 256, 1024), (17, 256, 1536), (8, 1024, 3584)])
+def test_k_split_matches_unsplit(M, N, K):
+    """With a workspace for the partial sums the few-row bf16 GEMM splits K;
+    given none it runs unsplit.  Exact inputs give identical bits either way,
+    random inputs agree within fp32 summation order (and with the oracle)."""
+    import ctypes
+    from block_scaled_precision_amd import moe_mx as m
+    L = m.lib()
+    need = m.mx_gemm_workspace_bytes(M, N, K, "bf16", "e2m1")
+    assert need >= 2 * M * N * 4, "this shape is expected to split K"
+
+    def run(a, w, s, ws):
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        st = L.mx_gemm(ctypes.c_void_p(a.data_ptr()), None, M, N, K, 0, ctypes.c_void_p(w.data_ptr()),
+                       ctypes.c_void_p(s.data_ptr()), 1, ctypes.c_float(1.0), ctypes.c_void_p(c.data_ptr()),
+                       ctypes.c_void_p(ws.data_ptr()) if ws is not None else None,
+                       ws.numel() if ws is not None else 0, None)
+        assert st == 0, m.status_str(st) if hasattr(m, "status_str") else st
+        return c
+
+    print_flush(f"mx_gemm K split vs unsplit M={M} N={N} K={K}")
+    a, w, s = (t.cuda() for t in _exact_inputs(M, N, K, "e2m1", 4))
+    ws = torch.empty((need,), dtype=torch.uint8, device="cuda")
+    c_split, c_plain = run(a, w, s, ws), run(a, w, s, None)
+    torch.cuda.synchronize()
+    assert torch.equal(c_split.view(torch.int16), c_plain.view(torch.int16))
+    a = gen.normal((M, K), 0, 24).to(torch.bfloat16).cuda()
+    wq, sq = m.mx_quantize(gen.normal((N, K), 0, 25, std=0.02).cuda(), "e2m1")
+    c_split, c_plain = run(a, wq, sq, ws), run(a, wq, sq, None)
+    torch.cuda.synchronize()
+    d = (c_split.float() - c_plain.float()).abs().max().item()
+    assert d <= 2e-2 * c_plain.float().abs().max().item()
+    ref = og.mx_gemm(a.double().cpu().numpy(), wq.cpu().numpy(), sq.cpu().numpy(), wfmt="e2m1", act="bf16")
+    assert_y_close(c_split.float().cpu().numpy(), ref, f"split {M}x{N}x{K}")
