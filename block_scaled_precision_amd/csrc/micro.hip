@@ -1,9 +1,11 @@
-// Small-batch path of the routed MoE layer (bf16 activations, E2M1 weights,
-// at most 8 tokens and 64 assignments): two kernels instead of five.
+// Fused small-batch path of the routed MoE layer (bf16 activations, E2M1
+// weights, at most 8 tokens and 64 assignments), taken on request: two
+// kernels instead of the default path's four (routing with the permutation,
+// FC1, FC2, combine).
 //
 // The mxfp6-sm120 page ("Execution model") runs batches of a few tokens on a
 // separate path: allocation-free routing, a split W1 and a fused W2
-// routed/shared reduction.  Here:
+// routed/shared reduction.  Here (without the split of W1, see below):
 //
 // k_micro_fc1  Every workgroup routes the batch itself in LDS (top-k of each
 //              token by one wave, then the active local experts in ascending

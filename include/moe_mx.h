@@ -191,10 +191,11 @@ typedef struct {
 } moe_problem_t;
 
 /* Flags of moe_problem_t.
- * MOE_FLAG_FUSED_SMALL_BATCH: run the two-launch small-batch path
- *   (mxfp6-sm120 page, "Execution model": allocation-free routing, split W1,
- *   fused W2 routed/shared reduction): every FC1 workgroup routes the batch
- *   itself and FC2 adds the routed and shared outputs per token in fp32, so
+ * MOE_FLAG_FUSED_SMALL_BATCH: run the two-launch small-batch path (the
+ *   mxfp6-sm120 page, "Execution model", gives small batches a path of their
+ *   own with allocation-free routing and a fused W2 routed/shared
+ *   reduction): every FC1 workgroup routes the batch itself (no routing
+ *   launch) and FC2 adds the routed and shared outputs per token in fp32, so
  *   y is ONE bf16 rounding of the whole sum (the default path rounds each
  *   weighted expert row first).  Requires bf16 activations, E2M1 weights,
  *   T <= 8, T*k <= 64, H % 512 == 0, I and I_shared multiples of 256 and
