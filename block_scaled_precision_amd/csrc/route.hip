@@ -147,7 +147,7 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ hist, int n
       tiles[tstart + i] = tl;
     }
   }
-  if (e == 0 && bm > 0) *num_tiles = s_b[16 + 15];
+  if (e == 0 && bm > 0) *num_tiles = s_b[1023];
 }
 
 // sorted_assign[pos] = a and, if requested, sorted_w[pos] = w[a] (the routing

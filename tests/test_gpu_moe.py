@@ -16,6 +16,9 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a
 CASES = {
     "tiny_w4a16": gen.WORKLOADS["tiny_w4a16"],
     "decode_w4a16_small": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=64, H=512, I=256, E=48),
+    # more than one token block and more than 32 experts: the multi-block scan's totals
+    "decode_w4a16_e96": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=200, H=512, I=256, E=96),
+    "prefill_w4a8_e40": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=500, H=1024, I=512, E=40, k=4),
     # a few tokens: top-k and permutation in one launch (and the fused small-batch path on request)
     "decode_w4a16_t4": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=4, H=512, I=256, E=48),
     "prefill_w4a8_small": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=300, H=512, I=512, E=16, k=4),
