@@ -300,7 +300,7 @@ def _tp_slice(t, r, n, fmt, what):
 # TokenSpeed SiTU page, "Supported contract": a tensor-parallel rank holds a
 # slice of the intermediate size of every expert and returns a partial output
 # that the caller all-reduces
-@pytest.mark.parametrize("name,n", [("decode_w4a16_small", 2), ("prefill_w4a8_small", 4),
+@pytest.mark.parametrize("name,n", [("decode_w4a16_small", 2), ("decode_w4a16_t4", 2), ("prefill_w4a8_small", 4),
                                     ("w6a8_shared_small", 2), ("w4a8_wide_full_tail_fc1", 2)])
 def test_tensor_parallel_shards_sum_to_full_layer(name, n):
     w, gw, arrs, shared, x, logits, m = _prepare(name)
@@ -364,7 +364,8 @@ def test_graph_capture_and_replay(name, fused):
             assert_y_close(got.float().cpu().numpy(), ref["y"], f"{name} graph replay {rep}")
 
 
-@pytest.mark.parametrize("name", ["decode_w4a16_small", "prefill_w4a8_small", "w6a8_shared_small"])
+@pytest.mark.parametrize("name", ["decode_w4a16_small", "decode_w4a16_t4", "prefill_w4a8_small",
+                                  "w6a8_shared_small"])
 def test_precomputed_topk_matches_router(name):
     w, gw, arrs, shared, x, logits, m = _prepare(name)
     prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared)
@@ -378,7 +379,7 @@ def test_precomputed_topk_matches_router(name):
 
 # (case, experts per shard) over the small-M, tiled (with a shared expert)
 # and wide kernels; the shared expert, when there is one, is added by shard 0
-@pytest.mark.parametrize("name,L", [("decode_w4a16_small", 12), ("prefill_w4a8_small", 4),
+@pytest.mark.parametrize("name,L", [("decode_w4a16_small", 12), ("decode_w4a16_t4", 12), ("prefill_w4a8_small", 4),
                                     ("w6a8_shared_small", 8), ("w4a8_wide_multi_tile", 2)])
 def test_expert_shards_sum_to_full_layer(name, L):
     w, gw, arrs, shared, x, logits, m = _prepare(name)
