@@ -187,9 +187,9 @@ def time_workload(torch, np, m, gen, w, mw, args):
     wts = torch.empty((w.T, w.k), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
-        m.moe_fused(prob, x, mw, router_logits=logits, y=y, workspace=ws, topk_ids_out=ids,
-                    topk_w_out=wts, stream=stream, stage_events=events)
+    # arguments checked and marshalled once: a step costs the host only the C call
+    step = m.FusedCall(prob, x, mw, router_logits=logits, y=y, workspace=ws, topk_ids_out=ids, topk_w_out=wts,
+                       stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -313,9 +313,18 @@ def small_batches(torch, np, m, gen, mw, args, batches=(1, 2, 4, 8)):
         for path, fused in (("default", False), ("fused_small_batch", True)):
             prob = m.make_problem(T, w.H, w.I, w.E, w.k, w.wfmt, w.act, fused_small_batch=fused)
             ws = torch.empty((m.moe_fused_workspace_bytes(prob),), dtype=torch.uint8, device="cuda")
-            fn = lambda: m.moe_fused(prob, x, mw, router_logits=logits, y=y, workspace=ws,  # noqa: E731
-                                     topk_ids_out=ids)
+            # arguments marshalled once (the stream is the current one at each call,
+            # so that the same call can be captured)
+            fn = m.FusedCall(prob, x, mw, router_logits=logits, y=y, workspace=ws, topk_ids_out=ids)
             ms = event_median(torch, m, fn, args.steps, args.warmup)
+            # host time per call (enqueue only): below the GPU time, the calls
+            # queue up and the events time the GPU, not the host
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                fn()
+            host_us = (time.perf_counter() - t0) / args.steps * 1e6
+            torch.cuda.synchronize()
             y_eager = y.clone()
             ms_graph, g = graph_median(torch, m, fn, args.steps, args.warmup)
             torch.cuda.synchronize()
@@ -329,9 +338,10 @@ def small_batches(torch, np, m, gen, mw, args, batches=(1, 2, 4, 8)):
             gbs_g = wbytes / (ms_graph / 1e3) / 1e9
             row[path] = {"ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "weight_GB_per_s": gbs,
                          "hbm_frac": gbs / HBM_PEAK_GBS, "graph_ms_per_step": ms_graph,
-                         "graph_hbm_frac": gbs_g / HBM_PEAK_GBS}
+                         "graph_hbm_frac": gbs_g / HBM_PEAK_GBS, "host_us_per_call": host_us}
             log(f"# decode shapes T={T} {path}: {ms * 1e3:.1f} us ({ms_graph * 1e3:.1f} us as a graph replay), "
-                f"{work['active_experts']} experts, {gbs:.0f} GB/s of weights ({gbs_g:.0f} replayed)")
+                f"{work['active_experts']} experts, {gbs:.0f} GB/s of weights ({gbs_g:.0f} replayed); "
+                f"host {host_us:.1f} us per call")
         row.update(active_experts=work["active_experts"], weight_bytes=wbytes)
         out[str(T)] = row
     return out

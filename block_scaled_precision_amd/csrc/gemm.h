@@ -46,6 +46,22 @@ struct FcArgs {
   // [ksplit, dense_rows, N] instead of obuf; 0 or 1 = no split
   int ksplit;
   float* part;
+  // few-token FC1 on the small-M kernel (launch_fc_small_routed): every
+  // workgroup routes the batch itself from the router logits [T, E] (local
+  // experts [off, off + L)) instead of reading tiles, num_tiles and
+  // sorted_assign, and workgroup 0 writes the routing out as the routing and
+  // permutation kernels would: ids_out / w_out [T, k], offsets_out [L + 1],
+  // sorted_out / sorted_w_out (the permuted assignments and their weights),
+  // tiles_out and ntiles_out (one tile per active local expert)
+  const float* logits;
+  int T, E, off, L;
+  int32_t* ids_out;
+  float* w_out;
+  int32_t* offsets_out;
+  int32_t* sorted_out;
+  float* sorted_w_out;
+  Tile* tiles_out;
+  int32_t* ntiles_out;
 };
 
 // Columns of N covered by one wave of the stream kernels.
@@ -86,6 +102,13 @@ hipError_t launch_fc_wide(const FcArgs& p, bool fc1, int grid, hipStream_t st);
 // Requires K % kSmallK == 0.
 constexpr int kSmallK = 256;
 hipError_t launch_fc_small(const FcArgs& p, bool fc1, int grid, hipStream_t st);
+// FC1 of the small-M kernel with the routing of a batch of at most
+// kSmallRoutedTokens tokens and kSmallRoutedAssign assignments in its prologue
+// (p.logits and the routing outputs set; E <= kMaxExperts); the tile height is
+// kStreamRows, one tile per active local expert.
+constexpr int kSmallRoutedTokens = 16;
+constexpr int kSmallRoutedAssign = 128;
+hipError_t launch_fc_small_routed(const FcArgs& p, int grid, hipStream_t st);
 // y = bf16_RNE(alpha * sum over s of part[s]) for the ksplit partial sums of a
 // split dense GEMM, summed in ascending s; n4 = rows * N / 4 (N % 4 == 0)
 hipError_t launch_splitk_reduce(const float* part, int ksplit, int64_t n4, float alpha, uint16_t* y,

@@ -39,6 +39,7 @@
 #include "copy_ring.h"
 #include "gemm.h"
 #include "mx_device.h"
+#include "batch_route.h"
 
 namespace moe_mx {
 
@@ -79,6 +80,17 @@ template <int GS> struct SGroup {
   static_assert(GS * (NG - 1) >= NSTAGE - 1, "scale-group ring too short");
 };
 
+// Routing tables of the few-token FC1 (after the scale-group ring): tile j is
+// active local expert j (T <= 16 tokens, so one 16-row tile holds all its
+// rows), and the token of each permuted row (the activation row it gathers).
+struct RouteTables {
+  Tile tile[kSmallRoutedAssign];
+  int32_t tok[kSmallRoutedAssign];
+};
+constexpr int L_RT = L_SG + L_SG_SIZE;
+static_assert(L_RT + sizeof(RouteTables) <= 160 * 1024, "LDS");
+static_assert(kSmallRoutedTokens <= SBM && kSmallRoutedAssign <= kThreadsS, "one tile per expert, one thread per assignment");
+
 // weight tile: 16-B chunk c of row r at slot c ^ swz(r), so that 8 rows read
 // at the same chunk fall in 8 different 16-B bank groups
 __device__ __forceinline__ int wb_swz(int r) { return BROW == 64 ? ((r >> 1) & 3) : (r & 7); }
@@ -94,7 +106,9 @@ struct SSched {
   int q, Q, NB, S, nk, my_items, total;
 };
 
-__device__ __forceinline__ SGeom s_geom(const FcArgs& p, const SSched& sc, int li) {
+// RT: the tile list is the workgroup's own routing tables in LDS
+template <bool RT>
+__device__ __forceinline__ SGeom s_geom(const FcArgs& p, const SSched& sc, int li, const uint8_t* smem) {
   const int j = sc.q + li * sc.Q;
   const int ti = j / (sc.NB * sc.S), r = j % (sc.NB * sc.S);
   SGeom g;
@@ -104,6 +118,11 @@ __device__ __forceinline__ SGeom s_geom(const FcArgs& p, const SSched& sc, int l
     g.expert = 0;
     g.p0 = SBM * ti;
     g.rows = min(SBM, p.dense_rows - SBM * ti);
+  } else if (RT) {
+    const Tile t = ((const RouteTables*)(smem + L_RT))->tile[ti];  // the same word in every lane
+    g.expert = __builtin_amdgcn_readfirstlane(t.expert);
+    g.p0 = __builtin_amdgcn_readfirstlane(t.p0);
+    g.rows = __builtin_amdgcn_readfirstlane(t.rows);
   } else {
     const Tile t = load_tile(p.tiles, ti);
     g.expert = t.expert;
@@ -148,7 +167,7 @@ __device__ __forceinline__ void wait_ops(int n) {
 
 // ------------------------------------------------------------ multiply ---
 
-template <bool FC1, int GS>
+template <bool FC1, int GS, bool RT>
 __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc, uint8_t* smem) {
   using SG = SGroup<GS>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -158,7 +177,7 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
   const int t1 = FC1 ? SBN / 2 + 16 * w : 32 * w + 16;
   v4f acc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
   int ci = 0, cs = 0;
-  SGeom it = s_geom(p, sc, 0);
+  SGeom it = s_geom<RT>(p, sc, 0, smem);
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     wait_lgkm0();
     barrier();
@@ -253,13 +272,13 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
     acc[0] = (v4f){0.f, 0.f, 0.f, 0.f};
     acc[1] = (v4f){0.f, 0.f, 0.f, 0.f};
     cs = 0;
-    if (++ci < sc.my_items) it = s_geom(p, sc, ci);
+    if (++ci < sc.my_items) it = s_geom<RT>(p, sc, ci, smem);
   }
 }
 
 // -------------------------------------------------------- weight copies ---
 
-template <bool FC1, int GS>
+template <bool FC1, int GS, bool RT>
 __device__ __forceinline__ void small_weights(const FcArgs& p, const SSched& sc, uint8_t* smem) {
   using SG = SGroup<GS>;
   const int lane = threadIdx.x & 63, bw = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) - kWaveB);
@@ -271,7 +290,7 @@ __device__ __forceinline__ void small_weights(const FcArgs& p, const SSched& sc,
   const uint8_t* src[kBData];
   const uint8_t* ssrc[SG::COPIES];
   auto setup = [&](int li) {
-    const SGeom it = s_geom(p, sc, li);
+    const SGeom it = s_geom<RT>(p, sc, li, smem);
     const int64_t k0 = (int64_t)it.ks * sc.nk * SBK;  // first k of the item's range
     const uint8_t* wb = p.w + (int64_t)it.expert * p.w_estride + k0 / 2;
     const uint8_t* sb = p.w_scale + (int64_t)it.expert * p.ws_estride + k0 / 32;
@@ -325,7 +344,7 @@ __device__ __forceinline__ void small_weights(const FcArgs& p, const SSched& sc,
 
 // ---------------------------------------------------- activation copies ---
 
-template <bool FC1>
+template <bool FC1, bool RT>
 __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched& sc, uint8_t* smem) {
   const int lane = threadIdx.x & 63;
   const int K = p.K;
@@ -335,9 +354,14 @@ __device__ __forceinline__ void small_activations(const FcArgs& p, const SSched&
   constexpr int CPA = 2 * SBK / 16;      // 16-B chunks per activation row and stage
   const uint8_t* src[kACopiesS];
   auto setup = [&](int li) {
-    const SGeom it = s_geom(p, sc, li);
+    const SGeom it = s_geom<RT>(p, sc, li, smem);
     int tok[16];
-    if (gather) {
+    if (gather && RT) {
+      // the same words in every lane (entries past the tile are never used)
+      const int32_t* lt = ((const RouteTables*)(smem + L_RT))->tok;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) tok[q] = __builtin_amdgcn_readfirstlane(lt[min(it.p0 + q, kSmallRoutedAssign - 1)]);
+    } else if (gather) {
       const Dw16 ids = load_dw16(p.sorted_assign + it.p0);
 #pragma unroll
       for (int q = 0; q < 16; ++q) tok[q] = ids.v[q] / p.k;
@@ -396,9 +420,80 @@ __global__ __launch_bounds__(kThreadsS, 1) void k_fc_small(FcArgs p) {
   sc.total = sc.my_items * sc.nk;
   if (sc.total == 0) return;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w < kMulW) small_multiply<FC1, GS>(p, sc, smem);
-  else if (w < kWaveA) small_weights<FC1, GS>(p, sc, smem);
-  else small_activations<FC1>(p, sc, smem);
+  if (w < kMulW) small_multiply<FC1, GS, false>(p, sc, smem);
+  else if (w < kWaveA) small_weights<FC1, GS, false>(p, sc, smem);
+  else small_activations<FC1, false>(p, sc, smem);
+}
+
+// Routing of the batch in the prologue of the few-token FC1: every workgroup
+// routes it into LDS (scratch in the stage ring, which no copy has reached
+// yet: top-k, token masks and the expert scan of batch_route.h) and keeps the
+// tile list and the token of each permuted row; workgroup 0 also writes the
+// routing out, with the top-k and the expert offsets, exactly as the routing
+// and permutation kernels would.  Returns the number of tiles (active local
+// experts), uniform; ends with a barrier.
+template <int NS>
+__device__ int route_in_fc1(const FcArgs& p, uint8_t* smem) {
+  using R = BatchRoute<kSmallRoutedAssign>;
+  static_assert(sizeof(R) + 4 * (kMaxExperts + 1) <= L_SG, "routing scratch");
+  R& r = *(R*)smem;
+  int32_t* start = (int32_t*)(smem + sizeof(R));  // first permuted row of each local expert, [L + 1]
+  RouteTables& rt = *(RouteTables*)(smem + L_RT);
+  route_batch<NS, kThreadsS>(p.logits, nullptr, nullptr, p.T, p.E, p.k, p.off, p.L, r, start);
+  const bool pub = blockIdx.x == 0;
+  for (int j = threadIdx.x; j < r.nact; j += kThreadsS) {
+    Tile t;
+    t.expert = r.act_e[j];
+    t.p0 = r.act_off[j];
+    t.rows = r.act_off[j + 1] - r.act_off[j];  // at most T <= 16: one tile per expert
+    t.pad = 0;
+    rt.tile[j] = t;
+    if (pub) p.tiles_out[j] = t;
+  }
+  const int A = p.T * p.k;
+  for (int a = threadIdx.x; a < A; a += kThreadsS) {
+    if (pub) {
+      p.ids_out[a] = r.ids[a];
+      p.w_out[a] = r.wts[a];
+    }
+    const int el = r.ids[a] - p.off;
+    if (el < 0 || el >= p.L) continue;
+    // rows of an expert are its tokens in ascending order
+    const int t = a / p.k;
+    const int pos = start[el] + __popc(r.mask[el] & ((1u << t) - 1u));
+    rt.tok[pos] = t;
+    if (pub) {
+      p.sorted_out[pos] = a;
+      p.sorted_w_out[pos] = r.wts[a];
+    }
+  }
+  if (pub) {
+    for (int e = threadIdx.x; e <= p.L; e += kThreadsS) p.offsets_out[e] = start[e];
+    if (threadIdx.x == 0) *p.ntiles_out = r.nact;
+  }
+  const int n = __builtin_amdgcn_readfirstlane(r.nact);
+  __syncthreads();  // the tables are complete and the scratch is free for the stage ring
+  return n;
+}
+
+template <int GS, int NS>
+__global__ __launch_bounds__(kThreadsS, 1) void k_fc_small_routed(FcArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[L_RT + sizeof(RouteTables)];
+  const int ntiles = route_in_fc1<NS>(p, smem);
+  SSched sc;
+  sc.S = 1;
+  sc.nk = p.K / SBK;
+  sc.NB = p.nchunks;
+  sc.q = blockIdx.x;
+  sc.Q = gridDim.x;
+  const int nitems = ntiles * sc.NB;
+  sc.my_items = nitems > sc.q ? (nitems - sc.q + sc.Q - 1) / sc.Q : 0;
+  sc.total = sc.my_items * sc.nk;
+  if (sc.total == 0) return;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (w < kMulW) small_multiply<true, GS, true>(p, sc, smem);
+  else if (w < kWaveA) small_weights<true, GS, true>(p, sc, smem);
+  else small_activations<true, true>(p, sc, smem);
 }
 
 template <bool FC1>
@@ -441,6 +536,27 @@ hipError_t launch_splitk_reduce(const float* part, int ksplit, int64_t n4, float
 hipError_t launch_fc_small(const FcArgs& p, bool fc1, int grid, hipStream_t st) {
   if (grid < 1) grid = 1;
   return fc1 ? launch_small_t<true>(p, grid, st) : launch_small_t<false>(p, grid, st);
+}
+
+template <int GS>
+static hipError_t launch_small_routed_t(const FcArgs& p, int grid, hipStream_t st) {
+  // key slots per lane of the top-k: the fewest of 1, 2, 4, 6, 8, 16 covering E
+  const int ns = (p.E + 63) / 64;
+  if (ns <= 1) k_fc_small_routed<GS, 1><<<grid, kThreadsS, 0, st>>>(p);
+  else if (ns <= 2) k_fc_small_routed<GS, 2><<<grid, kThreadsS, 0, st>>>(p);
+  else if (ns <= 4) k_fc_small_routed<GS, 4><<<grid, kThreadsS, 0, st>>>(p);
+  else if (ns <= 6) k_fc_small_routed<GS, 6><<<grid, kThreadsS, 0, st>>>(p);
+  else if (ns <= 8) k_fc_small_routed<GS, 8><<<grid, kThreadsS, 0, st>>>(p);
+  else k_fc_small_routed<GS, 16><<<grid, kThreadsS, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fc_small_routed(const FcArgs& p, int grid, hipStream_t st) {
+  if (grid < 1) grid = 1;
+  const int nk = p.K / SBK;
+  if (nk % 4 == 0) return launch_small_routed_t<4>(p, grid, st);
+  if (nk % 2 == 0) return launch_small_routed_t<2>(p, grid, st);
+  return launch_small_routed_t<1>(p, grid, st);
 }
 
 }  // namespace moe_mx

@@ -53,7 +53,7 @@
 #include "internal.h"
 #include "micro.h"
 #include "mx_device.h"
-#include "topk_device.h"
+#include "batch_route.h"
 
 namespace moe_mx {
 
@@ -62,18 +62,9 @@ namespace {
 constexpr int kWaves = 8;  // k_micro_fc2, and the routing of k_micro_fc1
 constexpr int kThreads = 64 * kWaves;
 constexpr int kThreads1 = 256;  // k_micro_fc1: four waves, one per 16 h columns of an item
-constexpr int kMaxL = kMaxExperts;
 
 // LDS routing state of one workgroup (k_micro_fc1)
-struct Route {
-  int32_t ids[kMicroMaxAssign];
-  float wts[kMicroMaxAssign];
-  uint32_t mask[kMaxL];      // token mask of each local expert
-  int32_t act_e[kMaxL];      // active experts, ascending
-  int32_t act_off[kMaxL + 1];
-  int32_t part[kThreads];    // scan partials
-  int32_t nact;
-};
+using Route = BatchRoute<kMicroMaxAssign>;
 static_assert(sizeof(Route) <= kMicroFc1StaticLds, "routing state");
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *(const uint4*)p; }
@@ -94,77 +85,6 @@ __device__ __forceinline__ void mma8(v4f& acc, uint32_t w, float sc, const uint4
 
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
-}
-
-// Block-wide exclusive scan of (active, count) over the L local experts;
-// fills act_e / act_off / nact.  Each thread owns ceil(L/kThreads)
-// consecutive experts.
-template <int NT>
-__device__ void scan_experts(Route& r, int L) {
-  const int tid = threadIdx.x;
-  const int per = (L + NT - 1) / NT;
-  const int e0 = tid * per;
-  int na = 0, nc = 0;
-  for (int e = e0; e < min(e0 + per, L); ++e) {
-    const int c = __popc(r.mask[e]);
-    na += c > 0;
-    nc += c;
-  }
-  r.part[tid] = (na << 16) | nc;  // at most 1024 experts and 64 assignments
-  __syncthreads();
-  for (int d = 1; d < NT; d <<= 1) {
-    const int v = tid >= d ? r.part[tid - d] : 0;
-    __syncthreads();
-    r.part[tid] += v;
-    __syncthreads();
-  }
-  int pa = (r.part[tid] >> 16) - na, pc = (r.part[tid] & 0xffff) - nc;
-  for (int e = e0; e < min(e0 + per, L); ++e) {
-    const int c = __popc(r.mask[e]);
-    if (c > 0) {
-      r.act_e[pa] = e;
-      r.act_off[pa] = pc;
-      ++pa;
-      pc += c;
-    }
-  }
-  if (tid == NT - 1) {
-    r.nact = r.part[tid] >> 16;
-    r.act_off[r.nact] = r.part[tid] & 0xffff;
-  }
-  __syncthreads();
-}
-
-// Routing of the batch into LDS (every workgroup does the same, bit for bit).
-template <int NS, int NT>
-__device__ void route_batch(const MicroArgs& p, Route& r) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int A = p.T * p.k;
-  if (p.ids_in) {
-    for (int i = threadIdx.x; i < A; i += NT) {
-      r.ids[i] = p.ids_in[i];
-      r.wts[i] = p.w_in[i];
-    }
-  } else {
-    for (int t = wv; t < p.T; t += NT / 64) {
-      TopkToken<NS> tk(p.logits + (int64_t)t * p.E, p.E, lane);
-      int my_e;
-      float my_v;
-      tk.select(p.E, 0, p.k, lane, my_e, my_v);
-      if (lane < p.k) {
-        r.ids[t * p.k + lane] = my_e;
-        r.wts[t * p.k + lane] = expf(my_v - tk.top) * (1.0f / tk.sum);
-      }
-    }
-  }
-  for (int e = threadIdx.x; e < p.L; e += NT) r.mask[e] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < A; i += NT) {
-    const int e = r.ids[i] - p.off;
-    if (e >= 0 && e < p.L) atomicOr(&r.mask[e], 1u << (i / p.k));
-  }
-  __syncthreads();
-  scan_experts<NT>(r, p.L);
 }
 
 // Publish the routing (workgroup 0): the caller's top-k outputs, and for
@@ -294,7 +214,8 @@ __global__ __launch_bounds__(kThreads1, 1) void k_micro_fc1(MicroArgs p) {
     const int t = i / chunks, c = i - t * chunks;
     *(uint4*)(xl + t * xs + 16 * c) = *(const uint4*)((const uint8_t*)p.x + ((int64_t)t * p.H + 8 * c) * 2);
   }
-  route_batch<NS, kThreads1>(p, r);  // ends with a barrier
+  route_batch<NS, kThreads1>(p.ids_in ? nullptr : p.logits, p.ids_in, p.w_in, p.T, p.E, p.k, p.off, p.L, r,
+                             nullptr);  // ends with a barrier
   if (blockIdx.x == 0) publish<kThreads1>(p, r);
 
   const int nb1 = p.I / 64;

@@ -667,9 +667,16 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   Tile* tiles = (Tile*)(ws + f.tiles);
   int32_t* ntiles = (int32_t*)(ws + f.ntiles);
   float* sorted_w = (float*)(ws + f.sorted_w);
-  // a few tokens: top-k and the permutation in one workgroup
-  const bool fused_route = !t->topk_ids_in && T <= kSmallFusedRouteTokens && k <= 64;
-  if (fused_route) {
+  // a few tokens on the small-M kernel: its FC1 routes the batch itself (no
+  // routing launch); otherwise, for a few tokens, top-k and the permutation in
+  // one workgroup
+  const bool route_in_fc1 = !t->topk_ids_in && !mx && f.routed == Fc::kSmall && T <= kSmallRoutedTokens &&
+                            (int64_t)T * k <= kSmallRoutedAssign;
+  const bool fused_route = !route_in_fc1 && !t->topk_ids_in && T <= kSmallFusedRouteTokens && k <= 64;
+  if (route_in_fc1) {
+    ids = t->topk_ids_out ? t->topk_ids_out : (int32_t*)(ws + f.ids);
+    wts = t->topk_w_out ? t->topk_w_out : (float*)(ws + f.w);
+  } else if (fused_route) {
     int32_t* ids_w = t->topk_ids_out ? t->topk_ids_out : (int32_t*)(ws + f.ids);
     float* w_w = t->topk_w_out ? t->topk_w_out : (float*)(ws + f.w);
     if (!ok(launch_route_permute_small(t->router_logits, T, p->E, k, ids_w, w_w, f.off, f.L,
@@ -693,7 +700,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   }
   // 2. permutation by local expert + tile list (done above for a few tokens)
   if (!mark(MOE_STAGE_PERMUTE)) return MOE_ERR_HIP;
-  if (!fused_route &&
+  if (!fused_route && !route_in_fc1 &&
       !ok(launch_permute(ids, wts, T, k, f.off, f.L, (int32_t*)(ws + f.hist), (int32_t*)(ws + f.rank),
                          (int32_t*)(ws + f.offsets), sorted, sorted_w, tiles, ntiles, f.bm, stream)))
     return MOE_ERR_HIP;
@@ -741,10 +748,27 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
       default: return launch_fc_stream(a, fc1, mx, wf, stream);
     }
   };
-  if (!ok(launch_fc(a1, true, f.routed, f.bm))) return MOE_ERR_HIP;
+  if (route_in_fc1) {
+    a1.logits = t->router_logits;
+    a1.T = T;
+    a1.E = p->E;
+    a1.off = f.off;
+    a1.L = f.L;
+    a1.ids_out = (int32_t*)ids;
+    a1.w_out = (float*)wts;
+    a1.offsets_out = (int32_t*)(ws + f.offsets);
+    a1.sorted_out = sorted;
+    a1.sorted_w_out = sorted_w;
+    a1.tiles_out = tiles;
+    a1.ntiles_out = ntiles;
+    if (!ok(launch_fc_small_routed(a1, cus, stream))) return MOE_ERR_HIP;
+  } else if (!ok(launch_fc(a1, true, f.routed, f.bm))) {
+    return MOE_ERR_HIP;
+  }
   // 6-7. FC2 + weighted combine into the fp32 accumulator
   if (!mark(MOE_STAGE_FC2)) return MOE_ERR_HIP;
   FcArgs a2 = a1;
+  a2.logits = nullptr;
   a2.a = ws + f.h;
   a2.a_scale = (const uint8_t*)(ws + f.hsc);
   a2.w = t->w2;
@@ -765,6 +789,7 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
     const int rows1 = st ? dense_tiled_rows(T, Is, true, tgrid) : f.shared_bm;
     const int rows2 = st ? dense_tiled_rows(T, H, false, tgrid) : f.shared_bm;
     FcArgs s1 = a1;
+    s1.logits = nullptr;
     s1.dense_rows = T;
     s1.w = t->ws1;
     s1.w_scale = t->ws1_scale;

@@ -58,11 +58,13 @@ struct TopkToken {
   float top = 0.f, sum = 0.f;
 
   __device__ __forceinline__ TopkToken(const float* row, int E, int lane) {
+    // every slot loads (past E from the last logit, then dropped), so that the
+    // loads are issued together and waited for once
+    float v[NS];
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      const int e = lane + 64 * i;
-      key[i] = e < E ? ordered_bits(row[e]) : 0u;
-    }
+    for (int i = 0; i < NS; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) key[i] = lane + 64 * i < E ? ordered_bits(v[i]) : 0u;
   }
   // slots j0 .. j0+jn-1 (jn <= 64): lane jj gets slot j0+jj's expert and logit
   __device__ __forceinline__ void select(int E, int j0, int jn, int lane, int& my_e, float& my_v) {

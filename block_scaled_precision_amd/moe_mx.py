@@ -372,6 +372,47 @@ def moe_fused(problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, router_
     return y
 
 
+class FusedCall:
+    """moe_fused with its arguments checked and marshalled once, for loops
+    that call the layer many times on the same buffers (their contents may
+    change between calls): each call then costs the host only the C call
+    itself.  The stream is the current one at each call unless one is given.
+    Calling returns y."""
+
+    def __init__(self, problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, router_logits=None,
+                 topk_ids_in=None, topk_w_in=None, y=None, workspace=None, topk_ids_out=None,
+                 topk_w_out=None, stream=None):
+        if y is None:
+            y = torch.empty((problem.T, problem.H), dtype=torch.bfloat16, device=x.device)
+        need = moe_fused_workspace_bytes(problem)
+        if workspace is None:
+            workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+        check_fused_args(problem, x, weights, router_logits, topk_ids_in, topk_w_in, y, workspace,
+                         topk_ids_out, topk_w_out)
+        self.y = y
+        # the tensors stay referenced for as long as the call can run
+        self._keep = (problem, x, weights, router_logits, topk_ids_in, topk_w_in, workspace, topk_ids_out,
+                      topk_w_out)
+        self._t = MoeTensors(*(None if v is None else v.data_ptr() for v in (
+            x, router_logits, topk_ids_in, topk_w_in, weights.w1, weights.w1_scale, weights.w2,
+            weights.w2_scale, weights.ws1, weights.ws1_scale, weights.ws2, weights.ws2_scale, y,
+            topk_ids_out, topk_w_out)), None)
+        self._p = ctypes.byref(problem)
+        self._tp = ctypes.byref(self._t)
+        self._ws = _ptr(workspace)
+        self._wsn = workspace.numel()
+        self._stream = None if stream is None else _stream(stream)
+        self._fn = lib().moe_fused
+
+    def __call__(self, stage_events=None):
+        self._t.stage_events = None if stage_events is None else ctypes.cast(stage_events, ctypes.c_void_p)
+        st = self._stream if self._stream is not None else _stream(None)
+        status = self._fn(self._p, self._tp, self._ws, self._wsn, st)
+        if status != MOE_OK:
+            raise MoeError(status, "moe_fused")
+        return self.y
+
+
 def moe_fused_noalloc(problem: MoeProblem, x: torch.Tensor, weights: MoeWeights, y: torch.Tensor,
                       router_logits=None, topk_ids_in=None, topk_w_in=None, topk_ids_out=None,
                       topk_w_out=None, stream=None):

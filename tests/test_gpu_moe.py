@@ -21,6 +21,11 @@ CASES = {
     "prefill_w4a8_e40": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=500, H=1024, I=512, E=40, k=4),
     # a few tokens: top-k and permutation in one launch (and the fused small-batch path on request)
     "decode_w4a16_t4": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=4, H=512, I=256, E=48),
+    # the small-M FC1 routing the batch itself: one token over 384 experts (six
+    # top-k key slots per lane, scale groups of 4 stages), and 16 tokens with
+    # 128 assignments (its limits)
+    "decode_w4a16_t1_e384": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=1, H=1024, I=256, E=384),
+    "decode_w4a16_t16": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=16, H=512, I=512, E=64),
     "prefill_w4a8_small": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=300, H=512, I=512, E=16, k=4),
     "skew_w4a16_small": gen.scaled(gen.WORKLOADS["skew_w4a16"], T=256, H=256, I=256, E=32, k=4),
     "w6a8_shared_small": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=100, H=512, I=512, E=24, k=6,
@@ -375,6 +380,51 @@ def test_precomputed_topk_matches_router(name):
     torch.cuda.synchronize()
     ref = _oracle_y(w, arrs, shared, x, None, topk_ids=ids.cpu().numpy(), topk_w=wts.cpu().numpy())
     assert_y_close(y, ref["y"], f"precomputed {name}")
+
+
+# few tokens on the small-M kernel: FC1 routes the batch in its prologue
+@pytest.mark.parametrize("name,shard", [("decode_w4a16_t4", None), ("decode_w4a16_t1_e384", None),
+                                        ("decode_w4a16_t16", None), ("decode_w4a16_t4", (12, 12)),
+                                        ("decode_w4a16_t1_e384", (100, 200))])
+def test_routing_in_fc1_matches_routing_kernels(name, shard):
+    """The routing that the few-token FC1 computes itself (top-k outputs,
+    the expert offsets and permuted assignments it leaves in the workspace)
+    and the layer output equal, bit for bit, those of the path that takes the
+    routing kernels' top-k as input; and y is within the bar of the oracle."""
+    w, gw, arrs, shared, x, logits, m = _prepare(name)
+    off, L = shard if shard else (0, 0)
+    if shard:
+        sl = slice(off, off + L)
+        gw = m.MoeWeights(gw.w1[sl], gw.w1_scale[sl], gw.w2[sl], gw.w2_scale[sl], w.wfmt)
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=0, local_offset=off, local_count=L)
+    ids, wts, _, _ = m.moe_route(logits.cuda(), w.k)
+    need = m.moe_fused_workspace_bytes(prob)
+    runs = {}
+    for how in ("logits", "topk_in"):
+        ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")
+        ids_o = torch.full((w.T, w.k), -1, dtype=torch.int32, device="cuda")
+        w_o = torch.full((w.T, w.k), -1.0, dtype=torch.float32, device="cuda")
+        print_flush(f"moe_fused {name} shard {shard}: routing from {how}")
+        if how == "logits":
+            y = m.moe_fused(prob, x.cuda(), gw, router_logits=logits.cuda(), workspace=ws, topk_ids_out=ids_o,
+                            topk_w_out=w_o)
+        else:
+            y = m.moe_fused(prob, x.cuda(), gw, topk_ids_in=ids, topk_w_in=wts, workspace=ws, topk_ids_out=ids_o,
+                            topk_w_out=w_o)
+        torch.cuda.synchronize()
+        nl = L if shard else w.E
+        o = m.moe_fused_workspace_offset(prob, "expert_offsets")
+        offs = ws[o:o + 4 * (nl + 1)].cpu().numpy().view(np.int32)
+        o = m.moe_fused_workspace_offset(prob, "sorted_assign")
+        sa = ws[o:o + 4 * int(offs[-1])].cpu().numpy().view(np.int32)
+        runs[how] = (y.cpu(), ids_o.cpu(), w_o.cpu(), offs, sa)
+    (y1, i1, w1, o1, s1), (y2, i2, w2, o2, s2) = runs["logits"], runs["topk_in"]
+    assert torch.equal(i1, ids.cpu()) and torch.equal(w1, wts.cpu())
+    assert torch.equal(i2, ids.cpu()) and torch.equal(w2, wts.cpu())
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+    assert torch.equal(y1, y2)
+    ref = _oracle_y(w, arrs, None, x, logits, local_offset=off, local_count=L if shard else None)
+    assert_y_close(y1.float().numpy(), ref["y"], f"routed FC1 {name}")
 
 
 # (case, experts per shard) over the small-M, tiled (with a shared expert)
