@@ -52,7 +52,7 @@ BOUND = {
 }
 # FC1 kernel that bench times per workload (the dominant kernel of the layer)
 FC1_KERNEL = {
-    "tiny_w4a16": "k_fc_small<true, 1>",
+    "tiny_w4a16": "k_fc_small_routed<1, 1>",  # 16 tokens: FC1 routes the batch itself
     "decode_w4a16": "k_fc_small<true, 4>",
     "prefill_w4a8": "k_fc_wide<true, 0>",
     "skew_w4a16": "k_fc_mid<true, 128>",
@@ -62,8 +62,8 @@ FC1_KERNEL = {
 # Sources of the GEMM kernels: a committed HBM-traffic summary counts only
 # while these are unchanged since it was taken.
 KERNEL_SOURCES = tuple(f"block_scaled_precision_amd/csrc/{f}" for f in (
-    "copy_ring.h", "gemm.h", "gemm_mid.hip", "gemm_small.hip", "gemm_stream.hip", "gemm_tiled.hip", "gemm_wide.hip",
-    "internal.h", "mx_device.h", "tiled_count.h", "wide_count.h"))
+    "batch_route.h", "copy_ring.h", "gemm.h", "gemm_mid.hip", "gemm_small.hip", "gemm_stream.hip", "gemm_tiled.hip",
+    "gemm_wide.hip", "internal.h", "mx_device.h", "tiled_count.h", "topk_device.h", "wide_count.h"))
 
 
 def parse():

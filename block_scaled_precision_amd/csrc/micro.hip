@@ -1,7 +1,7 @@
 // Fused small-batch path of the routed MoE layer (bf16 activations, E2M1
 // weights, at most 8 tokens and 64 assignments), taken on request: two
-// kernels instead of the default path's four (routing with the permutation,
-// FC1, FC2, combine).
+// kernels instead of the default path's three (FC1 with the routing in its
+// prologue, FC2, combine).
 //
 // The mxfp6-sm120 page ("Execution model") runs batches of a few tokens on a
 // separate path: allocation-free routing, a split W1 and a fused W2
