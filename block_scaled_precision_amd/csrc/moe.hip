@@ -668,10 +668,10 @@ extern "C" moe_status_t moe_fused(const moe_problem_t* p, const moe_tensors_t* t
   int32_t* ntiles = (int32_t*)(ws + f.ntiles);
   float* sorted_w = (float*)(ws + f.sorted_w);
   // a few tokens on the small-M kernel: its FC1 routes the batch itself (no
-  // routing launch); otherwise, for a few tokens, top-k and the permutation in
-  // one workgroup
+  // routing launch; k <= 64: one 64-lane selection round per token);
+  // otherwise, for a few tokens, top-k and the permutation in one workgroup
   const bool route_in_fc1 = !t->topk_ids_in && !mx && f.routed == Fc::kSmall && T <= kSmallRoutedTokens &&
-                            (int64_t)T * k <= kSmallRoutedAssign;
+                            k <= 64 && (int64_t)T * k <= kSmallRoutedAssign;
   const bool fused_route = !route_in_fc1 && !t->topk_ids_in && T <= kSmallFusedRouteTokens && k <= 64;
   if (route_in_fc1) {
     ids = t->topk_ids_out ? t->topk_ids_out : (int32_t*)(ws + f.ids);

@@ -231,8 +231,8 @@ typedef struct {
 /* Stages of moe_fused, in launch order, for stage_events.  A stage that a
  * problem does not need (x quantization with bf16 activations, the shared
  * expert without one) still records its event and takes no time.  A batch of
- * at most 16 tokens and 128 assignments with bf16 activations (E2M1 weights,
- * router logits given) is routed and permuted inside FC1: the route and
+ * at most 16 tokens and 128 assignments (k <= 64) with bf16 activations (E2M1
+ * weights, router logits given) is routed and permuted inside FC1: the route and
  * permute stages then take no time and FC1's includes them. */
 enum {
   MOE_STAGE_ROUTE = 0,     /* top-k routing (or copy of the given top-k)                        */

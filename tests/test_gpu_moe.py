@@ -26,6 +26,9 @@ CASES = {
     # 128 assignments (its limits)
     "decode_w4a16_t1_e384": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=1, H=1024, I=256, E=384),
     "decode_w4a16_t16": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=16, H=512, I=512, E=64),
+    # one token routed to 100 of 100 experts: more slots than one 64-lane
+    # selection round, so the routing kernels route it
+    "decode_w4a16_t1_k100": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=1, H=512, I=256, E=100, k=100),
     "prefill_w4a8_small": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=300, H=512, I=512, E=16, k=4),
     "skew_w4a16_small": gen.scaled(gen.WORKLOADS["skew_w4a16"], T=256, H=256, I=256, E=32, k=4),
     "w6a8_shared_small": gen.scaled(gen.WORKLOADS["w6a8_shared"], T=100, H=512, I=512, E=24, k=6,
