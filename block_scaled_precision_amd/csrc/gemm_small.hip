@@ -89,7 +89,7 @@ struct RouteTables {
 };
 constexpr int L_RT = L_SG + L_SG_SIZE;
 static_assert(L_RT + sizeof(RouteTables) <= 160 * 1024, "LDS");
-static_assert(kSmallRoutedTokens <= SBM && kSmallRoutedAssign <= kThreadsS, "one tile per expert, one thread per assignment");
+static_assert(kSmallRoutedTokens <= SBM && kSmallRoutedTokens <= 32, "one tile per expert, 32-bit token masks");
 
 // weight tile: 16-B chunk c of row r at slot c ^ swz(r), so that 8 rows read
 // at the same chunk fall in 8 different 16-B bank groups
@@ -178,6 +178,14 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
   v4f acc[2] = {(v4f){0.f, 0.f, 0.f, 0.f}, (v4f){0.f, 0.f, 0.f, 0.f}};
   int ci = 0, cs = 0;
   SGeom it = s_geom<RT>(p, sc, 0, smem);
+  // routed FC2: the item's row metadata, loaded when the item starts (scalar
+  // cache) so that its epilogue does not wait for it
+  const bool routed2 = !FC1 && p.dense_rows == 0;
+  Dw16 m_ids = {}, m_wts = {};
+  if (routed2) {
+    m_ids = load_dw16(p.sorted_assign + it.p0);
+    m_wts = load_dw16(p.sorted_w + it.p0);
+  }
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     wait_lgkm0();
     barrier();
@@ -246,8 +254,8 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
       } else {
         // row metadata of the tile through the scalar cache (16 entries from p0;
         // entries past the tile are never used)
-        const Dw16 ids = load_dw16(p.sorted_assign + it.p0);
-        const Dw16 wts = load_dw16(p.sorted_w + it.p0);
+        const Dw16& ids = m_ids;
+        const Dw16& wts = m_wts;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           orow[i] = 0;
@@ -272,7 +280,13 @@ __device__ __forceinline__ void small_multiply(const FcArgs& p, const SSched& sc
     acc[0] = (v4f){0.f, 0.f, 0.f, 0.f};
     acc[1] = (v4f){0.f, 0.f, 0.f, 0.f};
     cs = 0;
-    if (++ci < sc.my_items) it = s_geom<RT>(p, sc, ci, smem);
+    if (++ci < sc.my_items) {
+      it = s_geom<RT>(p, sc, ci, smem);
+      if (routed2) {
+        m_ids = load_dw16(p.sorted_assign + it.p0);
+        m_wts = load_dw16(p.sorted_w + it.p0);
+      }
+    }
   }
 }
 

@@ -469,6 +469,25 @@ def test_shard_without_assignments_is_zero():
     assert torch.count_nonzero(y).item() == 0
 
 
+def test_few_token_shard_without_assignments_is_zero():
+    """The same for a few tokens, whose FC1 routes the batch itself: a shard
+    of experts with -inf logits (never selected) gets no tile, FC1 and FC2
+    run no item, and y is exactly zero."""
+    w, gw, arrs, shared, x, logits, m = _prepare("decode_w4a16_t4")
+    off, L = w.E - 8, 8
+    logits = logits.clone()
+    logits[:, off:] = float("-inf")
+    shard = m.MoeWeights(gw.w1[off:], gw.w1_scale[off:], gw.w2[off:], gw.w2_scale[off:], w.wfmt)
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, local_offset=off, local_count=L)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    y = torch.full((w.T, w.H), 7.0, dtype=torch.bfloat16, device="cuda")
+    print_flush("moe_fused few-token shard of unselected experts")
+    m.moe_fused(prob, x.cuda(), shard, router_logits=logits.cuda(), topk_ids_out=ids, y=y)
+    torch.cuda.synchronize()
+    assert not ((ids.cpu().numpy() >= off).any())
+    assert torch.count_nonzero(y).item() == 0
+
+
 def test_zero_tokens_is_noop():
     w, gw, arrs, shared, x, logits, m = _prepare("tiny_w4a16")
     prob = m.make_problem(0, w.H, w.I, w.E, w.k, w.wfmt, w.act)
