@@ -202,6 +202,25 @@ __device__ __forceinline__ void mid_multiply(const FcArgs& p, const MSched& sc, 
     for (int n = 0; n < 8; ++n) acc[m][n] = (v4f){0.f, 0.f, 0.f, 0.f};
   int ci = 0, cs = 0;
   MGeom it = m_geom<TM>(p, sc, 0);
+  // routed FC2: the lane's row metadata for the item (output row and routing
+  // weight of rows 32 wr + 16 m + 4 g + i), loaded when the item starts so
+  // that the epilogue does not wait for it (rows past the tile read row 0)
+  int m_row[2][4];
+  float m_wt[2][4];
+  auto load_meta = [&]() {
+    if (!FC1 && p.dense_rows == 0) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = 32 * wr + 16 * m + 4 * g + i;
+          const int64_t pr = it.p0 + (row < it.rows ? row : 0);
+          m_row[m][i] = p.sorted_assign[pr];
+          m_wt[m][i] = p.sorted_w[pr];
+        }
+    }
+  };
+  load_meta();
   for (int gidx = 0; gidx < sc.total; ++gidx) {
     wait_lgkm0();
     barrier();
@@ -240,8 +259,8 @@ __device__ __forceinline__ void mid_multiply(const FcArgs& p, const MSched& sc, 
               int64_t orow = it.p0 + row;
               float wt = p.dense_weight;
               if (p.dense_rows == 0) {
-                orow = p.sorted_assign[it.p0 + row];
-                wt = p.sorted_w[it.p0 + row];
+                orow = m_row[m][i];
+                wt = m_wt[m][i];
               }
               uint16_t* o = p.obuf + orow * p.N + it.nb * MBN + 128 * wc + r16;
 #pragma unroll
@@ -255,7 +274,10 @@ __device__ __forceinline__ void mid_multiply(const FcArgs& p, const MSched& sc, 
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[m][n] = (v4f){0.f, 0.f, 0.f, 0.f};
     cs = 0;
-    if (++ci < sc.my_items) it = m_geom<TM>(p, sc, ci);
+    if (++ci < sc.my_items) {
+      it = m_geom<TM>(p, sc, ci);
+      load_meta();
+    }
   }
 }
 
