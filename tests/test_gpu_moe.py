@@ -488,6 +488,24 @@ def test_few_token_shard_without_assignments_is_zero():
     assert torch.count_nonzero(y).item() == 0
 
 
+@pytest.mark.parametrize("name", ["decode_w4a16_t4", "w6a8_shared_small"])
+def test_prepared_call_matches_moe_fused(name):
+    """FusedCall (arguments checked and marshalled once) gives the bits of
+    moe_fused, also after new contents are written into the same buffers."""
+    w, gw, arrs, shared, x, logits, m = _prepare(name)
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared)
+    xg, lg = x.cuda(), logits.cuda()
+    call = m.FusedCall(prob, xg, gw, router_logits=lg)
+    print_flush(f"FusedCall {name}")
+    for _ in range(2):
+        y = call().clone()
+        y_ref = m.moe_fused(prob, xg, gw, router_logits=lg)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+        xg.copy_(torch.flip(xg, [0]))
+        lg.copy_(torch.flip(lg, [1]))
+
+
 def test_zero_tokens_is_noop():
     w, gw, arrs, shared, x, logits, m = _prepare("tiny_w4a16")
     prob = m.make_problem(0, w.H, w.I, w.E, w.k, w.wfmt, w.act)
