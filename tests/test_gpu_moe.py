@@ -26,6 +26,10 @@ CASES = {
     # 128 assignments (its limits)
     "decode_w4a16_t1_e384": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=1, H=1024, I=256, E=384),
     "decode_w4a16_t16": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=16, H=512, I=512, E=64),
+    # FC1 routing with one expert per token, and with E not a multiple of 64
+    # (four key slots per lane, the last partly past E)
+    "decode_w4a16_t16_k1": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=16, H=512, I=256, E=8, k=1),
+    "decode_w4a16_t3_e200": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=3, H=512, I=256, E=200, k=6),
     # one token routed to 100 of 100 experts: more slots than one 64-lane
     # selection round, so the routing kernels route it
     "decode_w4a16_t1_k100": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=1, H=512, I=256, E=100, k=100),
@@ -388,7 +392,8 @@ def test_precomputed_topk_matches_router(name):
 # few tokens on the small-M kernel: FC1 routes the batch in its prologue
 @pytest.mark.parametrize("name,shard", [("decode_w4a16_t4", None), ("decode_w4a16_t1_e384", None),
                                         ("decode_w4a16_t16", None), ("decode_w4a16_t4", (12, 12)),
-                                        ("decode_w4a16_t1_e384", (100, 200))])
+                                        ("decode_w4a16_t1_e384", (100, 200)), ("decode_w4a16_t16_k1", None),
+                                        ("decode_w4a16_t3_e200", None), ("decode_w4a16_t3_e200", (50, 120))])
 def test_routing_in_fc1_matches_routing_kernels(name, shard):
     """The routing that the few-token FC1 computes itself (top-k outputs,
     the expert offsets and permuted assignments it leaves in the workspace)
