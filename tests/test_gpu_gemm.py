@@ -151,3 +151,34 @@ def test_k_split_matches_unsplit(M, N, K):
     assert d <= 2e-2 * c_plain.float().abs().max().item()
     ref = og.mx_gemm(a.double().cpu().numpy(), wq.cpu().numpy(), sq.cpu().numpy(), wfmt="e2m1", act="bf16")
     assert_y_close(c_split.float().cpu().numpy(), ref, f"split {M}x{N}x{K}")
+
+
+def _draw_exact(n, seed=20261204):
+    """Seeded random dense problems with exact inputs: any M, N a multiple of
+    8 and K of 128 (K <= 4096 keeps every E3M2 partial sum, a multiple of
+    1/16, inside fp32's 24 bits), either format and activation mode."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(rng.choice([1, 2, 7, 16, 17, 31, 33, 64, 100, 191, 193, 300, 600]))
+        N = 8 * int(rng.integers(1, 129))
+        K = 128 * int(rng.integers(1, 33))
+        fmt = str(rng.choice(["e2m1", "e3m2"]))
+        act = str(rng.choice(["bf16", "mxfp8"]))
+        cases.append(pytest.param(M, N, K, fmt, act, id=f"{i}_{M}x{N}x{K}_{fmt}_{act}"))
+    return cases
+
+
+@pytest.mark.parametrize("M,N,K,fmt,act", _draw_exact(32))
+def test_random_exact_gemm_is_bit_identical(M, N, K, fmt, act):
+    """Randomly drawn shapes, so that the dispatch meets sizes nobody picked
+    for it; exact inputs, so the output must equal the oracle bit for bit."""
+    from block_scaled_precision_amd import moe_mx as m
+    a, w, s = _exact_inputs(M, N, K, fmt, 5)
+    print_flush(f"mx_gemm random exact M={M} N={N} K={K} {fmt}/{act}")
+    c = m.mx_gemm(a.cuda(), w.cuda(), s.cuda(), fmt, act)
+    torch.cuda.synchronize()
+    ref = mx.round_to_bf16(og.mx_gemm(a.double().numpy(), w.numpy(), s.numpy(), wfmt=fmt, act=act))
+    got = c.float().cpu().numpy().astype(np.float64)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"{bad.size} of {got.size} differ, first at {np.unravel_index(bad[0], got.shape)}"
