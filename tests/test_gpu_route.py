@@ -49,6 +49,28 @@ def test_ties_and_shapes(T, E, k):
     _check(logits, k)
 
 
+def _draw(n, seed=20261205):
+    """Seeded random routing problems: T, E and k anywhere in the supported
+    range, half of them with logits on a coarse grid (many exact ties)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        T = int(rng.choice([1, 2, 3, 8, 15, 16, 17, 31, 64, 65, 127, 500, 1000, 2049]))
+        E = int(rng.integers(1, 1025))
+        k = int(rng.integers(1, min(E, 160) + 1))
+        ties = bool(rng.random() < 0.5)
+        cases.append(pytest.param(T, E, k, ties, i, id=f"{i}_T{T}_E{E}_k{k}" + ("_ties" if ties else "")))
+    return cases
+
+
+@pytest.mark.parametrize("T,E,k,ties,i", _draw(32))
+def test_random_shapes(T, E, k, ties, i):
+    g = torch.Generator().manual_seed(1000 + i)
+    logits = (torch.randint(-4, 5, (T, E), generator=g) * 0.5).float() if ties else torch.randn((T, E), generator=g)
+    print_flush(f"moe_route random T={T} E={E} k={k} ties={ties}")
+    _check(logits, k)
+
+
 def test_minus_inf_and_empty():
     g = torch.Generator().manual_seed(3)
     logits = torch.randn((100, 40), generator=g)
