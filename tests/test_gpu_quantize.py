@@ -108,3 +108,34 @@ def test_weight_tensor_of_tiny_layer():
         gc, gs = _gpu_quant(a, "e2m1")
         oc, os_ = _oracle_quant(a, "e2m1")
         assert np.array_equal(gs, os_) and np.array_equal(gc, oc)
+
+
+def _draw(n, seed=20261206):
+    """Seeded random shapes: 1-3000 rows, any multiple of 32 columns up to
+    5120, a row stride of the columns or wider, either source type, every
+    format."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        rows = int(rng.choice([1, 2, 5, 31, 64, 100, 257, 1000, 3000]))
+        cols = 32 * int(rng.integers(1, 161))
+        pad = int(rng.choice([0, 0, 8, 32, 96]))
+        fmt = str(rng.choice(FMTS))
+        dtype = str(rng.choice(["bf16", "fp32"]))
+        cases.append(pytest.param(rows, cols, pad, fmt, dtype, i, id=f"{i}_{rows}x{cols}+{pad}_{fmt}_{dtype}"))
+    return cases
+
+
+@pytest.mark.parametrize("rows,cols,pad,fmt,dtype,i", _draw(32))
+def test_random_shapes(rows, cols, pad, fmt, dtype, i):
+    from block_scaled_precision_amd import moe_mx as m
+    g = torch.Generator().manual_seed(2000 + i)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    big = (torch.randn((rows, cols + pad), generator=g)
+           * torch.exp2(torch.randint(-20, 20, (rows, 1), generator=g).float())).to(td)
+    print_flush(f"mx_quantize random {rows}x{cols} (row stride {cols + pad}) {fmt} {dtype}")
+    gc, gs = m.mx_quantize(big.cuda()[:, :cols], fmt)
+    torch.cuda.synchronize()
+    oc, os_ = _oracle_quant(big[:, :cols].contiguous(), fmt)
+    assert np.array_equal(gs.cpu().numpy(), os_)
+    assert np.array_equal(gc.cpu().numpy(), oc)
