@@ -189,3 +189,42 @@ def test_fused_small_batch_rejects_what_it_cannot_take():
     prob = m.make_problem(9, BASE.H, BASE.I, BASE.E, BASE.k, BASE.wfmt, BASE.act, fused_small_batch=True)
     with pytest.raises(m.MoeError, match="unsupported"):
         m.moe_fused(prob, x, gw, router_logits=logits)
+
+
+def _draw(n, seed=20261207):
+    """Seeded random problems inside the path's limits: 1-8 tokens with at
+    most 64 assignments, H a multiple of 512, I and I_shared of 256, every
+    gated activation, a shared expert in half of them."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        T = int(rng.integers(1, 9))
+        E = int(rng.choice([1, 5, 16, 64, 200]))
+        k = int(rng.integers(1, min(E, 64 // T, 8) + 1))
+        H = 512 * int(rng.integers(1, 5))
+        I = 256 * int(rng.integers(1, 5))
+        Is = int(rng.choice([0, 256 * int(rng.integers(1, 4))]))
+        act_fn = str(rng.choice(["silu", "relu2", "swiglu_oai"]))
+        w = gen.Workload(f"micro_random{i}", T, H, I, E, k, "e2m1", "bf16", I_shared=Is)
+        cases.append(pytest.param(w, act_fn, id=f"{i}_T{T}_H{H}_I{I}_E{E}_k{k}_Is{Is}_{act_fn}"))
+    return cases
+
+
+@pytest.mark.parametrize("w,act_fn", _draw(16))
+def test_random_problem(w, act_fn):
+    from block_scaled_precision_amd import moe_mx as m
+    gw = gpu_weights(w)
+    ow = oracle_weights(w)
+    arrs = [np.stack([ow[e][i] for e in range(w.E)]) for i in range(4)]
+    x = gen.hidden_states(w)
+    logits = gen.router_logits(w)
+    prob = m.make_problem(w.T, w.H, w.I, w.E, w.k, w.wfmt, w.act, I_shared=w.I_shared, act_fn=act_fn,
+                          fused_small_batch=True)
+    ids = torch.empty((w.T, w.k), dtype=torch.int32, device="cuda")
+    print_flush(f"small batch random {w.name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} Is={w.I_shared} {act_fn}")
+    y = m.moe_fused(prob, x.cuda(), gw, router_logits=logits.cuda(), topk_ids_out=ids)
+    torch.cuda.synchronize()
+    ref = om.moe_forward(x.double().numpy(), logits.numpy(), *arrs, k=w.k, wfmt=w.wfmt, act=w.act,
+                         shared=ow.get("shared"), act_fn=act_fn)
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    assert_y_close(y.float().cpu().numpy(), ref["y"], w.name)
