@@ -13,9 +13,8 @@ from tests.helpers import gpu_weights, print_flush
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not has_gpu(), reason="needs a GPU")]
 
-# decode-shaped (small-M kernel), a few tokens (top-k and permutation in one
-# launch; on request the fused small-batch path), and MXFP8 with a shared
-# expert (tiled kernel)
+# decode-shaped (small-M kernel), a few tokens (routing inside FC1; on request
+# the fused small-batch path), and MXFP8 with a shared expert (tiled kernel)
 CASES = {
     "decode": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=64, H=1024, I=512, E=32, k=8),
     "decode_few": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=8, H=1024, I=512, E=32, k=8),
