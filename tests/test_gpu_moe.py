@@ -19,7 +19,7 @@ CASES = {
     # more than one token block and more than 32 experts: the multi-block scan's totals
     "decode_w4a16_e96": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=200, H=512, I=256, E=96),
     "prefill_w4a8_e40": gen.scaled(gen.WORKLOADS["prefill_w4a8"], T=500, H=1024, I=512, E=40, k=4),
-    # a few tokens: top-k and permutation in one launch (and the fused small-batch path on request)
+    # a few tokens: routing inside FC1 (and the fused small-batch path on request)
     "decode_w4a16_t4": gen.scaled(gen.WORKLOADS["decode_w4a16"], T=4, H=512, I=256, E=48),
     # the small-M FC1 routing the batch itself: one token over 384 experts (six
     # top-k key slots per lane, scale groups of 4 stages), and 16 tokens with
