@@ -151,7 +151,7 @@ def test_layer_parity(name):
 
 # one case per kernel family: small-M, mid-M, tiled (+ shared), wide, stream
 @pytest.mark.parametrize("name", ["w4a16_small_gs4", "skew_w4a16_mid", "w6a8_shared_small",
-                                  "w4a8_wide_multi_tile", "w4a8_h384"])
+                                  "w4a8_wide_multi_tile", "w4a8_h384", "decode_w4a16_t4"])
 def test_repeat_is_bit_identical(name):
     """The same call twice gives the same bits: every output row has one
     writer and the combine adds the slots in a fixed order."""
